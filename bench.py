@@ -1,0 +1,245 @@
+"""Benchmark: column-wise-mask (FlashMask) attention forward + backward on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+fm_tile_bounds -> fm_fwd -> fm_bwd. The metric counts only unmasked FLOPs:
+    FLOP per step = 14 * d * U   (forward 4 d U: Q K^T and P V; backward 10 d U: the S recompute,
+                                  dP, dV, dK and dQ products), U = unmasked (query, key) pairs.
+The default workload is SFT packing with a causal document mask (B=1, H=32, N=8192, d=128, bf16).
+
+Prints one JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --no-cpu-baseline,
+--sweep (also time the other head-dim-128 workloads, a few steps each, reported under "sweep").
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "FlashMask fwd+bwd TFLOP/s (unmasked FLOPs) bf16 hd128; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+WORKLOADS = {
+    "sft_packing_causal_document": (2, "causal_document"),
+    "sft_packing_causal_window_1024": (2, "causal_window_1024"),
+    "dpo_rm_share_question": (3, "share_question"),
+    "dpo_rm_prefix_lm": (3, "prefix_lm"),
+    "dpo_rm_causal_key_drop": (3, "causal_key_drop"),
+    "long_context_causal_document": (4, "causal_document"),
+    "long_context_causal_document_window_4096": (4, "causal_document_window_4096"),
+    "long_context_causal_document_block_sparse": (4, "causal_document_block_sparse"),
+    "bert_base_full": (1, "full"),
+    "bert_base_causal": (1, "causal"),
+}
+DEFAULT_WORKLOAD = "sft_packing_causal_document"
+
+
+def unmasked_pairs(spec: W.MaskSpec, H: int) -> int:
+    """U by per-column interval union (inclusion-exclusion over at most three intervals)."""
+    N = spec.N
+    j = np.arange(N, dtype=np.int64)
+    zero = np.zeros(N, dtype=np.int64)
+    total = 0
+    for b in range(spec.B):
+        for hm in range(spec.Hm):
+            ivs = [(zero, j) if spec.causal else (zero, zero)]
+            for s, e in ((spec.lts, spec.lte), (spec.uts, spec.ute)):
+                if s is None:
+                    ivs.append((zero, zero))
+                else:
+                    s_ = np.clip(s[b, hm].astype(np.int64), 0, N)
+                    e_ = np.maximum(np.clip(e[b, hm].astype(np.int64), 0, N), s_)
+                    ivs.append((s_, e_))
+
+            def ln(a):
+                return np.maximum(a[1] - a[0], 0)
+
+            def meet(a, c):
+                return np.maximum(a[0], c[0]), np.minimum(a[1], c[1])
+
+            A, Bv, Cv = ivs
+            union = ln(A) + ln(Bv) + ln(Cv) - ln(meet(A, Bv)) - ln(meet(A, Cv)) - ln(meet(Bv, Cv)) \
+                + ln(meet(meet(A, Bv), Cv))
+            total += (N * N - int(union.sum())) * (H if spec.Hm == 1 else 1)
+    return total
+
+
+class Workload:
+    def __init__(self, name: str, device):
+        import torch
+        cfg_idx, mask = WORKLOADS[name]
+        cfg = W.CONFIGS[cfg_idx]
+        self.name, self.cfg, self.mask = name, cfg, mask
+        self.B, self.H, self.N, self.d = cfg.B, cfg.H, cfg.N, cfg.d
+        mi = cfg.masks.index(mask)
+        self.spec = W.make_mask(cfg.index, mask, cfg.B, cfg.H, cfg.N, mi)
+        self.mask_index = mi
+        q, k, v, do = W.make_tensors(cfg.index, mi, cfg.B, cfg.H, cfg.N, cfg.d)
+        self.host = (q, k, v, do)
+        to = lambda x: torch.from_numpy(x).to(device=device).to(torch.bfloat16)  # noqa: E731
+        self.q, self.k, self.v, self.do = (to(x) for x in (q, k, v, do))
+        self.vecs = [None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
+                     for x in self.spec.vectors()]
+        self.has_vecs = any(x is not None for x in self.vecs)
+        self.scale = 1.0 / math.sqrt(self.d)
+        self.U = unmasked_pairs(self.spec, self.H)
+        self.flop_fwd = 4.0 * self.d * self.U
+        self.flop_bwd = 10.0 * self.d * self.U
+        self.flop = self.flop_fwd + self.flop_bwd
+
+
+def time_workload(fm, wl: Workload, steps: int, warmup: int):
+    import torch
+    dev = wl.q.device
+    stream = torch.cuda.current_stream(dev)
+    bounds = torch.empty(fm.fm_bounds_elems(wl.B, wl.spec.Hm, wl.N) or 8, dtype=torch.int32, device=dev)
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
+    ws = torch.empty(fm.fm_bwd_workspace_bytes(torch.bfloat16, wl.B, wl.H, wl.N, wl.d), dtype=torch.uint8,
+                     device=dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        b = None
+        if wl.has_vecs:
+            b = fm.fm_tile_bounds(*wl.vecs, wl.B, wl.spec.Hm, wl.N, bounds=bounds)
+        if evs is not None:
+            evs[1].record(stream)
+        fm.fm_fwd(wl.q, wl.k, wl.v, *wl.vecs, bounds=b, causal=wl.spec.causal, scale=wl.scale, out=out, lse=lse)
+        if evs is not None:
+            evs[2].record(stream)
+        fm.fm_bwd(wl.q, wl.k, wl.v, out, wl.do, lse, *wl.vecs, bounds=b, causal=wl.spec.causal, scale=wl.scale,
+                  dq=dq, dk=dk, dv=dv, workspace=ws)
+        if evs is not None:
+            evs[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    parts = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in events])  # ms
+    ok = bool(torch.isfinite(out.float()).all() and torch.isfinite(dq.float()).all()
+              and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all())
+    return wall, parts.mean(axis=0), ok
+
+
+def cpu_baseline(wl: Workload, budget_heads: int):
+    """The oracle, as it stands, on the first heads of the same workload (bounded CPU sample)."""
+    import torch
+    from oracle import attention as OA
+    q, k, v, do = wl.host
+    heads = [(0, h) for h in range(min(wl.H, budget_heads))]
+    r = lambda x: torch.from_numpy(x[:, : len(heads)]).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
+    qs, ks, vs, dos = (r(x) for x in (q, k, v, do))
+    sub = W.MaskSpec(wl.N, 1, wl.spec.Hm if wl.spec.Hm == 1 else len(heads), wl.spec.causal,
+                     *[None if x is None else x[:1, : (1 if wl.spec.Hm == 1 else len(heads))]
+                       for x in wl.spec.vectors()])
+    workers = min(len(heads), 16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    _, _, _, _, _, used = OA.fwd_bwd(qs, ks, vs, dos, sub.vectors(), sub.causal, wl.scale, sub.Hm, workers=workers)
+    dt = time.perf_counter() - t0
+    U = unmasked_pairs(sub, len(heads))
+    flop = 14.0 * wl.d * U
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"{len(heads)} of {wl.H} heads of {wl.name} (fp64 NumPy fwd+bwd), {dt:.1f} s",
+            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--sweep", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mask_aware_exact_amd as fm
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fm.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = Workload(args.workload, dev)
+    wall, parts_ms, ok = time_workload(fm, wl, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
+    bwd_ms = float(parts_ms[2])
+    bwd_tflops = wl.flop_bwd / (bwd_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "mask": wl.mask,
+                   "causal": bool(wl.spec.causal), "unmasked_pairs": int(wl.U),
+                   "flop_per_step": wl.flop, "flop_formula": "14*d*U"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "parts_ms": {"fm_tile_bounds": round(float(parts_ms[0]), 4), "fm_fwd": round(float(parts_ms[1]), 4),
+                     "fm_bwd": round(bwd_ms, 4)},
+        "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[1] * 1e-3) / 1e12, 2),
+                         "fm_bwd": round(bwd_tflops, 2)},
+        "finite_outputs": ok,
+        "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_pre + bwd_main + bwd_dq launches)",
+                     "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+    if args.sweep:
+        sweep = {}
+        for name in WORKLOADS:
+            if name == wl.name or WORKLOADS[name][0] == 1:
+                continue
+            del wl
+            torch.cuda.empty_cache()
+            wl = Workload(name, dev)
+            w2, p2, ok2 = time_workload(fm, wl, max(3, args.steps // 4), 1)
+            ms = w2 * 1e3 / max(3, args.steps // 4)
+            sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
+                           "U": int(wl.U), "fwd_ms": round(float(p2[1]), 3), "bwd_ms": round(float(p2[2]), 3),
+                           "bounds_ms": round(float(p2[0]), 4), "finite": ok2}
+        rec["sweep"] = sweep
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

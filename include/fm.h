@@ -1,0 +1,127 @@
+/*
+ * fm.h -- C ABI of the column-wise-mask (FlashMask) exact attention library for AMD MI355X (gfx950).
+ *
+ * What is computed.  Exact softmax attention, forward and backward, under a column-wise sparse mask:
+ * each key column j carries four query-axis boundaries LTS_j, LTE_j, UTS_j, UTE_j (FlashMask abstract,
+ * papers.pytorch.kr 2410.01359: a column-wise sparse representation with O(N) memory; FlashMask-3
+ * summary, readmex.ai, abstract body: four query-axis boundary vectors, indexed by key position,
+ * storing query-axis interval boundaries). Query row i is masked for key column j when
+ *     (causal and i < j)  or  LTS_j <= i < LTE_j  or  UTS_j <= i < UTE_j
+ * (half-open intervals; an interval with start >= end is empty; values outside [0, N) are clipped
+ * by this set definition and are not an error). Masked scores are excluded from the softmax. A query
+ * row with every key masked yields out = 0, lse = -inf, a zero dq row and no dk/dv contribution.
+ *
+ * Tiles whose every (row, column) is masked are skipped and tiles with no masked entry run without
+ * the elementwise mask ("kernel optimizations that eliminate unnecessary computations by leveraging
+ * sparsity ... without sacrificing computational accuracy", FlashMask abstract). The result does not
+ * depend on the classification: it only decides which work is done.
+ *
+ * Conventions shared by every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library keeps no pointer after
+ *    a call returns, allocates nothing and keeps no state between calls.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and never synchronizes. Argument
+ *    errors are detected on the host before any launch, so a failing call launches nothing.
+ *  - Layout: q, k, v, out, dout, dq, dk, dv are contiguous row-major [B, H, N, d] of `dtype`
+ *    (self-attention: N queries and N keys, the same H for queries and keys). lse is float32
+ *    [B, H, N], natural log of the sum of exp(scale * q.k) over the unmasked keys.
+ *  - Mask vectors are contiguous int32 [B, Hm, N] with Hm = 1 (shared by all heads) or Hm = H.
+ *    A pair (LTS, LTE) or (UTS, UTE) may be NULL as a pair: that interval is empty. One NULL and one
+ *    non-NULL pointer in a pair is FM_ERR_INVALID.
+ *  - bounds is int32 [B, Hm, ceil(N / fm_kblock()), 8] as written by fm_tile_bounds for the same
+ *    vectors. It may be NULL only when all four vectors are NULL. Bounds that do not belong to the
+ *    vectors give wrong results but never out-of-range memory accesses.
+ *  - Outputs must not alias inputs or each other.
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_INVALID = 1,     /* NULL required pointer, B/H/N out of range, Hm not in {1, H}, half-NULL pair,
+                             non-finite scale, vectors without bounds, qblock not positive */
+  FM_ERR_UNSUPPORTED = 2, /* d not in {64, 128} or unknown dtype */
+  FM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fm_bwd_workspace_bytes() */
+  FM_ERR_LAUNCH = 4       /* the HIP runtime reported an error for a launch */
+} fm_status;
+
+typedef enum { FM_BF16 = 0, FM_F32 = 1 } fm_dtype;
+
+/* Largest N accepted by every call (row and column indices stay within int32 arithmetic). */
+#define FM_MAX_N (1 << 24)
+
+/* Width in key columns of one bounds entry (64). */
+int fm_kblock(void);
+
+/* Query rows per forward tile for head dim d (the qblock at which the forward kernel classifies
+   tiles), or 0 for an unsupported d. */
+int fm_fwd_qblock(int d);
+
+/* Number of int32 elements of the bounds array: B * Hm * ceil(N / kblock) * 8 (0 on bad sizes). */
+size_t fm_bounds_elems(int B, int Hm, int N);
+
+/* Per-key-tile bounds pre-pass.
+ * For each (b, hm, key tile t) over the valid columns c in [t*kblock, min(N, (t+1)*kblock)) writes
+ *   bounds[b][hm][t][0..7] = min LTS, max LTS, min LTE, max LTE, min UTS, max UTS, min UTE, max UTE.
+ * A NULL pair writes the canonical empty values: LT -> N, N, N, N; UT -> 0, 0, 0, 0.
+ * The pages name no such pass; it is the per-tile summary from which the tile classification is read.
+ * Errors: FM_ERR_INVALID (bounds NULL, sizes out of range, half-NULL pair). */
+fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute,
+                         int B, int Hm, int N, int32_t* bounds, hipStream_t stream);
+
+/* Forward pass (FlashMask abstract: exact attention with mask-driven skipping; FlashAttention-3
+ * abstract, fugumt.com 2407.08608: tiled online softmax).
+ *   out[b,h,i,:] = sum_j P_ij v[b,h,j,:],  P_ij = exp(S_ij - lse_i) on unmasked (i, j), 0 elsewhere,
+ *   S_ij = scale * q[b,h,i,:] . k[b,h,j,:],  lse[b,h,i] = log(sum over unmasked j of exp(S_ij)).
+ * Vectors for head h are read at [b, (Hm == H ? h : 0), :]. causal != 0 adds the i < j mask.
+ * bf16 inputs use bf16 matrix products with float32 accumulation and a float32 softmax; out is
+ * rounded to bf16 (nearest even). float32 inputs use float32 matrix products.
+ * Errors: FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_LAUNCH. */
+fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
+                 const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                 const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream);
+
+/* Device workspace fm_bwd needs: a float32 [B, H, N, d] dq accumulator plus a float32 [B, H, N] row
+ * term D_i = sum_k dout_ik out_ik, each 256-byte aligned. 0 on bad sizes. */
+size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d);
+
+/* Backward pass: gradients of sum(out * dout) with out from fm_fwd on the same inputs and mask.
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ * with P recomputed from q, k and the forward's lse. Key tiles run in parallel; each accumulates its
+ * dk/dv tile on chip and adds its dq contribution into the float32 workspace accumulator, which a
+ * final pass rounds into dq. dq, dk, dv have `dtype`. The workspace is overwritten (its previous
+ * content does not matter) and must not be shared by concurrent calls.
+ * Errors: FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_LAUNCH. */
+fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, fm_dtype dtype, int B, int H, int N, int d,
+                 const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                 const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Test hook: the tile classifier the kernels use, materialised. For each (b, hm, query tile of
+ * qblock rows, key tile of kblock columns), clipped to N, writes classes[b][hm][qt][kt]:
+ *   2 FULL    the causal triangle or one interval covers every (row, column) of the tile
+ *   0 NONE    not FULL, and neither the causal triangle nor either interval reaches any row of it
+ *   1 PARTIAL otherwise.
+ * With bounds read as (mnLTS, mxLTS, mnLTE, mxLTE, mnUTS, mxUTS, mnUTE, mxUTE) and rows [r0, r1),
+ * columns [c0, c1): causal FULL iff r1-1 < c0, causal NONE iff !causal or r0 >= c1-1;
+ * interval FULL iff r0 >= mxS and r1 <= mnE; interval NONE iff r1 <= mnS or r0 >= mxE.
+ * classes is uint8 [B, Hm, ceil(N/qblock), ceil(N/kblock)].
+ * Errors: FM_ERR_INVALID (NULL pointers, sizes, qblock <= 0), FM_ERR_LAUNCH. */
+fm_status fm_tile_classes(const int32_t* bounds, int B, int Hm, int N, int causal, int qblock,
+                          uint8_t* classes, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* fm_status_str(fm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FM_H */

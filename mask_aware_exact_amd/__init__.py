@@ -1,0 +1,191 @@
+"""Thin Python binding of libfm.so, the column-wise-mask (FlashMask) exact attention library for MI355X.
+
+Argument marshalling only: torch supplies device memory and the current stream, every step of the
+path runs in the HIP kernels behind the C ABI declared in include/fm.h. The entry points keep the C
+names: fm_tile_bounds, fm_fwd, fm_bwd (plus fm_tile_classes, a test hook). There is no fallback:
+if libfm.so is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfm.so")
+
+FM_OK, FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_LAUNCH = 0, 1, 2, 3, 4
+FM_BF16, FM_F32 = 0, 1
+NONE, PARTIAL, FULL = 0, 1, 2
+
+EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_fwd",
+            "fm_bwd_workspace_bytes", "fm_bwd", "fm_tile_classes", "fm_status_str")
+
+
+class FmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libfm.so and declare its signatures; raises if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mask_aware_exact_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fm_kblock.restype = I
+    lib.fm_kblock.argtypes = []
+    lib.fm_fwd_qblock.restype = I
+    lib.fm_fwd_qblock.argtypes = [I]
+    lib.fm_bounds_elems.restype = S
+    lib.fm_bounds_elems.argtypes = [I, I, I]
+    lib.fm_tile_bounds.restype = I
+    lib.fm_tile_bounds.argtypes = [P, P, P, P, I, I, I, P, P]
+    lib.fm_fwd.restype = I
+    lib.fm_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P]
+    lib.fm_bwd_workspace_bytes.restype = S
+    lib.fm_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fm_bwd.restype = I
+    lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P, P, S, P]
+    lib.fm_tile_classes.restype = I
+    lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
+    lib.fm_status_str.restype = ctypes.c_char_p
+    lib.fm_status_str.argtypes = [I]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().fm_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != FM_OK:
+        raise FmError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FM_BF16
+    if t.dtype == torch.float32:
+        return FM_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _vec(t):
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise TypeError("mask vectors must be int32")
+    return t
+
+
+def fm_kblock() -> int:
+    return load_library().fm_kblock()
+
+
+def fm_fwd_qblock(d: int) -> int:
+    return load_library().fm_fwd_qblock(int(d))
+
+
+def fm_bounds_elems(B: int, Hm: int, N: int) -> int:
+    return load_library().fm_bounds_elems(B, Hm, N)
+
+
+def fm_bwd_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int) -> int:
+    code = FM_BF16 if dtype == torch.bfloat16 else FM_F32 if dtype == torch.float32 else 99
+    return load_library().fm_bwd_workspace_bytes(code, B, H, N, d)
+
+
+def fm_tile_bounds(lts, lte, uts, ute, B: int, Hm: int, N: int, bounds=None, stream=None):
+    """int32 [B, Hm, ceil(N/64), 8] per-key-tile min/max of the four vectors (None pairs allowed)."""
+    lib = load_library()
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    _need_cuda(*vecs)
+    if bounds is None:
+        dev = next((x.device for x in vecs if x is not None), torch.device("cuda"))
+        bounds = torch.empty(fm_bounds_elems(B, Hm, N), dtype=torch.int32, device=dev)
+    _check(lib.fm_tile_bounds(*[_ptr(x) for x in vecs], B, Hm, N, _ptr(bounds), _stream(stream)),
+           "fm_tile_bounds")
+    return bounds.view(B, Hm, -1, 8)
+
+
+def fm_fwd(q, k, v, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False, scale=None,
+           out=None, lse=None, stream=None):
+    """(out, lse) for q, k, v of shape [B, H, N, d]; vectors int32 [B, Hm, N] or None."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, bounds, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.fm_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, N, d, *[_ptr(x) for x in vecs], Hm,
+                      _ptr(bounds), int(bool(causal)), float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "fm_fwd")
+    return out, lse
+
+
+def fm_bwd(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False,
+           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv): gradients of sum(out * dout)."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, out, dout, lse, bounds, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fm_bwd_workspace_bytes(q.dtype, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fm_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N, d,
+                      *[_ptr(x) for x in vecs], Hm, _ptr(bounds), int(bool(causal)), float(scale), _ptr(dq),
+                      _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)), "fm_bwd")
+    return dq, dk, dv
+
+
+def fm_tile_classes(bounds, B: int, Hm: int, N: int, causal: bool, qblock: int, classes=None, stream=None):
+    """uint8 [B, Hm, ceil(N/qblock), ceil(N/64)] tile classes (0 NONE, 1 PARTIAL, 2 FULL)."""
+    lib = load_library()
+    _need_cuda(bounds)
+    if qblock <= 0:
+        raise FmError(FM_ERR_INVALID, "fm_tile_classes")
+    nq, nk = -(-N // qblock), -(-N // 64)
+    if classes is None:
+        dev = bounds.device if bounds is not None else torch.device("cuda")
+        classes = torch.empty(B * Hm * nq * nk, dtype=torch.uint8, device=dev)
+    _check(lib.fm_tile_classes(_ptr(bounds), B, Hm, N, int(bool(causal)), qblock, _ptr(classes),
+                               _stream(stream)), "fm_tile_classes")
+    return classes.view(B, Hm, nq, nk)

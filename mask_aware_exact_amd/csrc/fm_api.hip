@@ -1,0 +1,138 @@
+// C ABI of the column-wise-mask attention library: argument validation and kernel launches.
+// Every argument check runs on the host before any HIP call, so a rejected call touches no device
+// state and launches nothing. See include/fm.h for the contract of each entry point.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fm.h"
+#include "fm_common.h"
+
+namespace fm {
+hipError_t launch_tile_bounds(const int* lts, const int* lte, const int* uts, const int* ute, int rows, int N,
+                              int* bounds, hipStream_t stream);
+hipError_t launch_tile_classes(const int* bounds, int rows, int N, int causal, int qblock, uint8_t* classes,
+                               hipStream_t stream);
+hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
+                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
+                      int N, int Hm, int causal, float scale, hipStream_t stream);
+hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* dd,
+                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B,
+                      int H, int N, int Hm, int causal, float scale, hipStream_t stream);
+int fwd_qblock();
+}  // namespace fm
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool sizes_ok(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0 || N > FM_MAX_N) return false;
+  // flattened grids and row counts stay far inside 32-bit launch limits
+  return (long long)B * H <= (1LL << 20) && (long long)B * H * ((N + 63) / 64) < (1LL << 31);
+}
+
+bool pair_ok(const int32_t* s, const int32_t* e) { return (s == nullptr) == (e == nullptr); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fm_status dtype_d_ok(fm_dtype dtype, int d) {
+  if (dtype != FM_BF16 && dtype != FM_F32) return FM_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+fm_status mask_args_ok(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                       int H, const int32_t* bounds) {
+  if (!pair_ok(lts, lte) || !pair_ok(uts, ute)) return FM_ERR_INVALID;
+  if (Hm != 1 && Hm != H) return FM_ERR_INVALID;
+  const bool any_vec = lts != nullptr || uts != nullptr;
+  if (any_vec && bounds == nullptr) return FM_ERR_INVALID;
+  return FM_OK;
+}
+
+fm_status from_hip(hipError_t e) { return e == hipSuccess ? FM_OK : FM_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fm_kblock(void) { return fm::KBLOCK; }
+
+int fm_fwd_qblock(int d) { return (d == 64 || d == 128) ? fm::fwd_qblock() : 0; }
+
+size_t fm_bounds_elems(int B, int Hm, int N) {
+  if (B <= 0 || Hm <= 0 || N <= 0 || N > FM_MAX_N) return 0;
+  return (size_t)B * Hm * ((N + fm::KBLOCK - 1) / fm::KBLOCK) * 8;
+}
+
+fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int B,
+                         int Hm, int N, int32_t* bounds, hipStream_t stream) {
+  if (bounds == nullptr || !sizes_ok(B, Hm, N)) return FM_ERR_INVALID;
+  if (!pair_ok(lts, lte) || !pair_ok(uts, ute)) return FM_ERR_INVALID;
+  return from_hip(fm::launch_tile_bounds(lts, lte, uts, ute, B * Hm, N, bounds, stream));
+}
+
+fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
+                 const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                 const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return FM_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !std::isfinite(scale)) return FM_ERR_INVALID;
+  fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
+  if (st != FM_OK) return st;
+  st = dtype_d_ok(dtype, d);
+  if (st != FM_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FM_ERR_INVALID;
+  return from_hip(fm::launch_fwd(dtype == FM_BF16, d, q, k, v, out, lse, lts, lte, uts, ute, bounds, B, H, N, Hm,
+                                 causal != 0, scale, stream));
+}
+
+size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d) {
+  if (dtype_d_ok(dtype, d) != FM_OK || !sizes_ok(B, H, N)) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts, const int32_t* lte,
+                 const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds, int causal, float scale,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return FM_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !std::isfinite(scale)) return FM_ERR_INVALID;
+  fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
+  if (st != FM_OK) return st;
+  st = dtype_d_ok(dtype, d);
+  if (st != FM_OK) return st;
+  const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FM_ERR_INVALID;
+  const size_t need = fm_bwd_workspace_bytes(dtype, B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FM_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * H * N;
+  float* dq_acc = static_cast<float*>(workspace);
+  float* dd = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * sizeof(float)));
+  return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts,
+                                 ute, bounds, B, H, N, Hm, causal != 0, scale, stream));
+}
+
+fm_status fm_tile_classes(const int32_t* bounds, int B, int Hm, int N, int causal, int qblock, uint8_t* classes,
+                          hipStream_t stream) {
+  if (classes == nullptr || qblock <= 0 || !sizes_ok(B, Hm, N)) return FM_ERR_INVALID;
+  return from_hip(fm::launch_tile_classes(bounds, B * Hm, N, causal != 0, qblock, classes, stream));
+}
+
+const char* fm_status_str(fm_status s) {
+  switch (s) {
+    case FM_OK: return "ok";
+    case FM_ERR_INVALID: return "invalid argument";
+    case FM_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
+    case FM_ERR_WORKSPACE: return "workspace missing or too small";
+    case FM_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

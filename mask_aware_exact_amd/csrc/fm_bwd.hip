@@ -1,0 +1,381 @@
+// Backward pass of exact attention under the column-wise mask (gfx950).
+//
+// The gradient of sum(out * dO) through softmax attention, recomputing P from q, k and the forward's
+// lse, with tiles the mask covers completely skipped (FlashMask abstract, papers.pytorch.kr
+// 2410.01359). Three kernels run in order on the caller's stream:
+//  1. bwd_pre:  D_i = sum_d dO_id out_id (float32) per row, and the float32 dq accumulator cleared.
+//  2. bwd_main: one workgroup per (b, h, key tile of BC = 128 columns); wave w owns keys 32 w .. 32 w+31
+//     (one key column per lane). Per query tile of BR rows that the mask does not cover completely:
+//       S = Q K^T and dP = dO V^T with K, V held in registers (keys as the N axis, so every lane keeps
+//       one key column and its four mask values in registers);
+//       P = exp(S - lse) (0 where masked), dS = P o (dP - D);
+//       dV^T += dO^T P and dK^T += Q^T dS, the k axis (query rows) read from the row-major Q / dO
+//       tiles through transposing LDS reads, accumulated on chip for the whole query loop;
+//       dS goes to LDS, and dQ_tile = dS K over the workgroup's 128 keys is added into the float32
+//       accumulator with hardware float atomics.
+//  3. bwd_dq:   dq = accumulator rounded to the input type.
+#include "fm_common.h"
+
+namespace fm {
+
+// ------------------------------------------------------------------ 1. D and accumulator clear
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ dout,
+                                                      float* __restrict__ dd, float* __restrict__ dq_acc,
+                                                      long rows) {
+  constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);      // elements per chunk
+  constexpr int RPB = 256 / CPR;                // rows per block
+  constexpr int ACC_CHUNKS = D * 4 / 16 / CPR;  // 16-byte accumulator chunks per lane
+  const int tid = threadIdx.x;
+  const long row = (long)blockIdx.x * RPB + tid / CPR;
+  const int c = tid % CPR;
+  float part = 0.f;
+  if (row < rows) {
+    const T* po = out + row * D + c * EPC;
+    const T* pd = dout + row * D + c * EPC;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) part += (float)po[e] * (float)pd[e];
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < ACC_CHUNKS; ++k)
+      *reinterpret_cast<f32x4*>(dq_acc + row * D + (c * ACC_CHUNKS + k) * 4) = z;
+  }
+#pragma unroll
+  for (int m = CPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+  if (row < rows && c == 0) dd[row] = part;
+}
+
+// ------------------------------------------------------------------ 2. main key-tile-parallel kernel
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* dd;
+  float* dq_acc;
+  void* dk;
+  void* dv;
+  const int* lts;
+  const int* lte;
+  const int* uts;
+  const int* ute;
+  const int* bounds;
+  int B, H, N, Hm;
+  int nkt;  // key tiles of BC per head
+  int nkb;  // bounds entries per (b, hm) row
+  int causal;
+  float scale;
+  float scale_log2;
+};
+
+template <typename T, int D>
+struct BwdTraits {
+  static constexpr int BC = 128;                         // keys per workgroup
+  static constexpr int BR = sizeof(T) == 2 ? 64 : 32;    // query rows per iteration
+  static constexpr int NT = 256;
+  static constexpr int PITCH = D + 16 / (int)sizeof(T);  // row-major Q / dO / K tiles
+  static constexpr int PS = BR + 16 / (int)sizeof(T);    // dS tile [key][row]
+  static constexpr int NKF = D / MM<T>::KW;              // K / V fragments per lane
+  static constexpr int NIB = BR / 32;                    // 32-row blocks per query tile
+  static constexpr int NDB = D / 32;                     // 32-wide d blocks
+  static constexpr int TPB = 16 / MM<T>::E;              // products per 32 k values
+  static constexpr int NQB = NIB * NDB;                  // dQ output blocks per query tile
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
+  using Tr = BwdTraits<T, D>;
+  using M = MM<T>;
+  constexpr int BC = Tr::BC, BR = Tr::BR, PITCH = Tr::PITCH, PS = Tr::PS;
+  __shared__ __attribute__((aligned(16))) T k_lds[BC * PITCH];
+  __shared__ __attribute__((aligned(16))) T q_lds[BR * PITCH];
+  __shared__ __attribute__((aligned(16))) T do_lds[BR * PITCH];
+  __shared__ __attribute__((aligned(16))) T ds_lds[BC * PS];
+  __shared__ __attribute__((aligned(16))) float lse_lds[BR];
+  __shared__ __attribute__((aligned(16))) float dd_lds[BR];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int kt = (int)(blockIdx.x / BH);  // early key tiles carry the most causal work: dispatch them first
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int hm = a.Hm > 1 ? h : 0;
+  const int N = a.N;
+  const int c0 = kt * BC;
+  const int c1 = min(N, c0 + BC);
+  const int jl = wave * 32 + l32;  // this lane's key column inside the tile
+  const int j = c0 + jl;
+
+  const size_t head = (size_t)bh * N * D;
+  const T* __restrict__ qg = static_cast<const T*>(a.q) + head;
+  const T* __restrict__ kg = static_cast<const T*>(a.k) + head;
+  const T* __restrict__ vg = static_cast<const T*>(a.v) + head;
+  const T* __restrict__ dog = static_cast<const T*>(a.dout) + head;
+  const float* __restrict__ lseg = a.lse + (size_t)bh * N;
+  const float* __restrict__ ddg = a.dd + (size_t)bh * N;
+  float* __restrict__ dqg = a.dq_acc + head;
+  const size_t vrow = ((size_t)b * a.Hm + hm) * N;
+  const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
+  const bool has_lt = a.lts != nullptr;
+  const bool has_ut = a.uts != nullptr;
+  const bool causal = a.causal != 0;
+
+  // This lane's key column: mask values and K / V fragments (k = d).
+  int m_lts = 0, m_lte = 0, m_uts = 0, m_ute = 0;
+  typename M::frag kf[Tr::NKF], vf[Tr::NKF];
+  if (j < N) {
+    if (has_lt) { m_lts = a.lts[vrow + j]; m_lte = a.lte[vrow + j]; }
+    if (has_ut) { m_uts = a.uts[vrow + j]; m_ute = a.ute[vrow + j]; }
+#pragma unroll
+    for (int c = 0; c < Tr::NKF; ++c) {
+      kf[c] = load_kcontig_frag<T>(kg + (size_t)j * D + c * M::KW + g * M::E);
+      vf[c] = load_kcontig_frag<T>(vg + (size_t)j * D + c * M::KW + g * M::E);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < Tr::NKF; ++c) {
+      kf[c] = typename M::frag{};
+      vf[c] = typename M::frag{};
+    }
+  }
+  load_tile<T, BC, D, PITCH, Tr::NT>(k_lds, kg, c0, N, tid);
+
+  f32x16 dk[Tr::NDB], dv[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  int bnd[8];
+  merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N, bnd);
+  const int nq = (N + BR - 1) / BR;
+  const int qt_begin = causal ? c0 / BR : 0;
+
+  for (int qt = qt_begin; qt < nq; ++qt) {
+    const int q0 = qt * BR;
+    const int q1 = min(N, q0 + BR);
+    const int cls = classify_tile(q0, q1, c0, c1, bnd, causal);
+    if (cls == CLS_FULL) continue;
+    const bool need_mask = (cls == CLS_PARTIAL) || (q1 - q0 < BR) || (c1 - c0 < BC);
+
+    __syncthreads();  // previous iteration's LDS reads are done
+    load_tile<T, BR, D, PITCH, Tr::NT>(q_lds, qg, q0, N, tid);
+    load_tile<T, BR, D, PITCH, Tr::NT>(do_lds, dog, q0, N, tid);
+    if (tid < BR) {
+      const int i = q0 + tid;
+      float l = i < N ? lseg[i] : INFINITY;
+      // a row without any unmasked key has lse = -inf; +inf makes exp(S - lse) = 0 for it
+      l = (l == -INFINITY) ? INFINITY : l;
+      lse_lds[tid] = l * LOG2E;
+      dd_lds[tid] = i < N ? ddg[i] : 0.f;
+    }
+    __syncthreads();
+
+    // S = Q K^T and dP = dO V^T: rows = this tile's queries, columns = this wave's keys.
+    f32x16 s[Tr::NIB], dp[Tr::NIB];
+#pragma unroll
+    for (int ib = 0; ib < Tr::NIB; ++ib) {
+      s[ib] = zero16();
+      dp[ib] = zero16();
+      const T* qrow = q_lds + (ib * 32 + l32) * PITCH + g * M::E;
+      const T* dorow = do_lds + (ib * 32 + l32) * PITCH + g * M::E;
+#pragma unroll
+      for (int c = 0; c < Tr::NKF; ++c) {
+        s[ib] = M::mma(load_kcontig_frag<T>(qrow + c * M::KW), kf[c], s[ib]);
+        dp[ib] = M::mma(load_kcontig_frag<T>(dorow + c * M::KW), vf[c], dp[ib]);
+      }
+    }
+
+    // P and dS in place (s <- P, dp <- dS).
+#pragma unroll
+    for (int ib = 0; ib < Tr::NIB; ++ib) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int il0 = ib * 32 + 8 * q4 + 4 * g;
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_lds + il0);
+        const f32x4 dd4 = *reinterpret_cast<const f32x4*>(dd_lds + il0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          float p = exp2f(s[ib][r] * a.scale_log2 - lse4[e]);
+          if (need_mask) {
+            const int i = q0 + il0 + e;
+            const bool msk = (i >= N) || (j >= N) ||
+                             masked_elem(i, j, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
+            p = msk ? 0.f : p;
+          }
+          s[ib][r] = p;
+          dp[ib][r] = p * (dp[ib][r] - dd4[e]);
+        }
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (k = query rows of the tile).
+#pragma unroll
+    for (int t = 0; t < Tr::NIB * Tr::TPB; ++t) {
+      const typename M::frag pf = acc_frag<T>(s[t / Tr::TPB], t % Tr::TPB);
+      const typename M::frag sf = acc_frag<T>(dp[t / Tr::TPB], t % Tr::TPB);
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        dv[db] = M::mma(load_kmajor_frag<T>(do_lds, PITCH, 0, db * 32, t, lane), pf, dv[db]);
+        dk[db] = M::mma(load_kmajor_frag<T>(q_lds, PITCH, 0, db * 32, t, lane), sf, dk[db]);
+      }
+    }
+
+    // dS to LDS as [key][row], rounded to T.
+#pragma unroll
+    for (int ib = 0; ib < Tr::NIB; ++ib) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int il0 = ib * 32 + 8 * q4 + 4 * g;
+        T* dst = ds_lds + jl * PS + il0;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)dp[ib][4 * q4 + e];
+          *reinterpret_cast<bf16x4*>(dst) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = dp[ib][4 * q4 + e];
+          *reinterpret_cast<f32x4*>(dst) = w;
+        }
+      }
+    }
+    __syncthreads();
+
+    // dQ tile += scale * dS K over the workgroup's keys; each wave owns some (row block, d block) pairs.
+    for (int ob = wave; ob < Tr::NQB; ob += 4) {
+      const int ib = ob / Tr::NDB;
+      const int db = ob % Tr::NDB;
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int t = 0; t < BC / 32 * Tr::TPB; ++t) {
+        const typename M::frag af = load_kmajor_frag<T>(ds_lds, PS, 0, ib * 32, t, lane);
+        const typename M::frag bfr = load_kmajor_frag<T>(k_lds, PITCH, 0, db * 32, t, lane);
+        acc = M::mma(af, bfr, acc);
+      }
+      const int d = db * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = q0 + ib * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (i < N) unsafeAtomicAdd(dqg + (size_t)i * D + d, acc[r] * a.scale);
+      }
+    }
+  }
+
+  // dK = scale * dK^T, dV = dV^T for this lane's key column.
+  if (j < N) {
+    T* dkg = static_cast<T*>(a.dk) + head + (size_t)j * D;
+    T* dvg = static_cast<T*>(a.dv) + head + (size_t)j * D;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 wk, wv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wk[e] = (bf16)(dk[db][4 * q4 + e] * a.scale);
+            wv[e] = (bf16)dv[db][4 * q4 + e];
+          }
+          *reinterpret_cast<bf16x4*>(dkg + d0) = wk;
+          *reinterpret_cast<bf16x4*>(dvg + d0) = wv;
+        } else {
+          f32x4 wk, wv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wk[e] = dk[db][4 * q4 + e] * a.scale;
+            wv[e] = dv[db][4 * q4 + e];
+          }
+          *reinterpret_cast<f32x4*>(dkg + d0) = wk;
+          *reinterpret_cast<f32x4*>(dvg + d0) = wv;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 3. dq = accumulator
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ acc, T* __restrict__ dq, long n4) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 v = *reinterpret_cast<const f32x4*>(acc + 4 * i);
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x4*>(dq + 4 * i) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(dq + 4 * i) = v;
+  }
+}
+
+// ------------------------------------------------------------------ host launch
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* dd,
+                               const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds,
+                               int B, int H, int N, int Hm, int causal, float scale, hipStream_t stream) {
+  const long rows = (long)B * H * N;
+  constexpr int CPR = D * (int)sizeof(T) / 16;
+  constexpr int RPB = 256 / CPR;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     static_cast<const T*>(out), static_cast<const T*>(dout), dd, dq_acc, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.dd = dd; a.dq_acc = dq_acc; a.dk = dk; a.dv = dv;
+  a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
+  a.B = B; a.H = H; a.N = N; a.Hm = Hm;
+  a.nkt = (N + BwdTraits<T, D>::BC - 1) / BwdTraits<T, D>::BC;
+  a.nkb = (N + KBLOCK - 1) / KBLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * LOG2E;
+  const long grid = (long)a.nkt * B * H;
+  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const long n4 = rows * D / 4;
+  hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, dq_acc,
+                     static_cast<T*>(dq), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* dd,
+                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B,
+                      int H, int N, int Hm, int causal, float scale, hipStream_t stream) {
+  if (bf16_in) {
+    if (d == 64)
+      return launch_bwd_t<bf16, 64>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
+                                    N, Hm, causal, scale, stream);
+    return launch_bwd_t<bf16, 128>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
+                                   N, Hm, causal, scale, stream);
+  }
+  if (d == 64)
+    return launch_bwd_t<float, 64>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
+                                   N, Hm, causal, scale, stream);
+  return launch_bwd_t<float, 128>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
+                                  N, Hm, causal, scale, stream);
+}
+
+}  // namespace fm

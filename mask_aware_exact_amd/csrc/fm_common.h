@@ -1,0 +1,184 @@
+// Device helpers shared by the column-wise-mask attention kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used throughout (measured on MI355X):
+//  * v_mfma_f32_32x32x16_bf16: operand A row = lane % 32, operand B column = lane % 32; the 8 slots of
+//    lanes 0-31 and of lanes 32-63 cover the 16 k values, identically for A and B.
+//  * accumulator: lane l, register r holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+//  * v_mfma_f32_32x32x2_f32: A row / B column = lane % 32, k = lane / 32, same accumulator layout.
+//  * ds_read_b64_tr_b16 over 16-lane groups: if lane s of a group addresses row k0 + s / 4, columns
+//    4 (s % 4) .. +3 of a row-major 16-bit tile, lane t of the group receives column t, rows k0 .. k0+3.
+//
+// An accumulator used as the k operand of the next product keeps its register order: slot s of
+// product t reads register r = t * E + s, i.e. k index 8 (r / 4) + 4 (l / 32) + r % 4. The other
+// operand of such a product is read from LDS in the same k order (see load_kmajor_frag).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KBLOCK = 64;  // key columns per bounds entry
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+enum TileClass : int { CLS_NONE = 0, CLS_PARTIAL = 1, CLS_FULL = 2 };
+
+// Tile rule: rows [r0, r1), columns [c0, c1), both already clipped to N; b = per-tile bounds
+// (mnLTS, mxLTS, mnLTE, mxLTE, mnUTS, mxUTS, mnUTE, mxUTE).
+__device__ __host__ inline int classify_tile(int r0, int r1, int c0, int c1, const int* b, bool causal) {
+  const bool causal_full = causal && (r1 - 1 < c0);
+  const bool causal_none = !causal || (r0 >= c1 - 1);
+  const bool lt_full = (r0 >= b[1]) && (r1 <= b[2]);
+  const bool lt_none = (r1 <= b[0]) || (r0 >= b[3]);
+  const bool ut_full = (r0 >= b[5]) && (r1 <= b[6]);
+  const bool ut_none = (r1 <= b[4]) || (r0 >= b[7]);
+  if (causal_full || lt_full || ut_full) return CLS_FULL;
+  if (causal_none && lt_none && ut_none) return CLS_NONE;
+  return CLS_PARTIAL;
+}
+
+// Bounds of key tiles [kt0, kt1) of one (b, hm) row merged by min/max; canonical empties when the
+// bounds array is absent (all vectors absent).
+__device__ inline void merged_bounds(const int* __restrict__ brow, int kt0, int kt1, int N, int* out) {
+  if (brow == nullptr) {
+    out[0] = out[1] = out[2] = out[3] = N;
+    out[4] = out[5] = out[6] = out[7] = 0;
+    return;
+  }
+  const int* p = brow + (size_t)kt0 * 8;
+  for (int e = 0; e < 8; ++e) out[e] = p[e];
+  for (int t = kt0 + 1; t < kt1; ++t) {
+    const int* q = brow + (size_t)t * 8;
+    for (int e = 0; e < 8; e += 2) {
+      out[e] = min(out[e], q[e]);
+      out[e + 1] = max(out[e + 1], q[e + 1]);
+    }
+  }
+}
+
+// Whether query row i is masked for a key column with the given vector values.
+__device__ __forceinline__ bool masked_elem(int i, int j, bool causal, bool has_lt, bool has_ut, int lts,
+                                            int lte, int uts, int ute) {
+  bool m = causal && (i < j);
+  m |= has_lt && (lts <= i) && (i < lte);
+  m |= has_ut && (uts <= i) && (i < ute);
+  return m;
+}
+
+// ------------------------------------------------------------------ matrix-core traits
+
+template <typename T>
+struct MM;
+
+template <>
+struct MM<bf16> {
+  static constexpr int E = 8;    // operand elements per lane
+  static constexpr int KW = 16;  // k extent of one instruction
+  using frag = bf16x8;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct MM<float> {
+  static constexpr int E = 1;
+  static constexpr int KW = 2;
+  using frag = float;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// E contiguous elements along k (the contiguous axis) at p: a k-contiguous operand fragment.
+template <typename T>
+__device__ __forceinline__ typename MM<T>::frag load_kcontig_frag(const T* p) {
+  return *reinterpret_cast<const typename MM<T>::frag*>(p);
+}
+
+// Operand fragment of product t whose k axis runs along the ROWS of a row-major LDS tile (pitch in
+// elements) and whose m/n index (lane % 32) runs along its columns starting at col0. k index of slot s
+// follows the accumulator register order (r = t * E + s -> 8 (r / 4) + 4 (lane / 32) + r % 4), offset by
+// row0. bf16 uses two transposing LDS reads; float reads one element.
+template <typename T>
+__device__ __forceinline__ typename MM<T>::frag load_kmajor_frag(const T* tile, int pitch, int row0, int col0,
+                                                               int t, int lane);
+
+template <>
+__device__ __forceinline__ bf16x8 load_kmajor_frag<bf16>(const bf16* tile, int pitch, int row0, int col0, int t,
+                                                        int lane) {
+  const int g = lane >> 5;
+  const int s = lane & 15;
+  const int col = col0 + (lane & 16) + 4 * (s & 3);
+  const int row = row0 + 16 * t + 4 * g + (s >> 2);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + row * pitch + col));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + (row + 8) * pitch + col));
+  bf16x8 f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+
+template <>
+__device__ __forceinline__ float load_kmajor_frag<float>(const float* tile, int pitch, int row0, int col0, int t,
+                                                        int lane) {
+  const int g = lane >> 5;
+  const int row = row0 + 8 * (t >> 2) + 4 * g + (t & 3);
+  return tile[row * pitch + col0 + (lane & 31)];
+}
+
+// Fragment of product t taken from an accumulator (registers t * E .. t * E + E - 1), rounded to T.
+template <typename T>
+__device__ __forceinline__ typename MM<T>::frag acc_frag(const f32x16& acc, int t);
+
+template <>
+__device__ __forceinline__ bf16x8 acc_frag<bf16>(const f32x16& acc, int t) {
+  bf16x8 f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f[s] = (bf16)acc[8 * t + s];
+  return f;
+}
+
+template <>
+__device__ __forceinline__ float acc_frag<float>(const f32x16& acc, int t) {
+  return acc[t];
+}
+
+// 16-byte global/LDS copy helpers.
+__device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }
+
+// Copy rows [row0, row0 + ROWS) of a [*, D] row-major global matrix into an LDS tile of pitch PITCH
+// elements, zero-filling rows at or past nrows. All NT threads of the block take part.
+template <typename T, int ROWS, int D, int PITCH, int NT>
+__device__ __forceinline__ void load_tile(T* lds, const T* __restrict__ g, int row0, int nrows, int tid) {
+  constexpr int CHUNKS_PER_ROW = D * (int)sizeof(T) / 16;
+  constexpr int TOTAL = ROWS * CHUNKS_PER_ROW;
+  static_assert(TOTAL % NT == 0, "tile copy must divide evenly");
+#pragma unroll
+  for (int it = 0; it < TOTAL / NT; ++it) {
+    const int c = it * NT + tid;
+    const int r = c / CHUNKS_PER_ROW;
+    const int cc = c % CHUNKS_PER_ROW;
+    i32x4 v = {0, 0, 0, 0};
+    if (row0 + r < nrows) v = ld16(reinterpret_cast<const char*>(g + (size_t)(row0 + r) * D) + cc * 16);
+    st16(reinterpret_cast<char*>(lds + r * PITCH) + cc * 16, v);
+  }
+}
+
+}  // namespace fm

@@ -1,0 +1,240 @@
+// Forward pass of exact attention under the column-wise mask (gfx950).
+//
+// Tiled online softmax as in FlashAttention (FlashAttention-3 abstract, fugumt.com 2407.08608; the
+// FlashAttention README on wenyanet.com), with tiles that the mask covers completely skipped and
+// tiles it does not touch run without the elementwise mask (FlashMask abstract,
+// papers.pytorch.kr 2410.01359).
+//
+// Work decomposition (a design for 64-wide waves and 32x32 matrix cores, not taken from the pages):
+//  * one workgroup = 4 waves = BR = 128 query rows of one (b, h); wave w owns rows 32 w .. 32 w + 31.
+//  * key tiles of BC = 64 columns (one bounds entry) are staged row-major in LDS.
+//  * each wave computes S^T = K Q^T (keys as the M axis, its 32 queries as the N axis), so that every
+//    lane holds one query row: the row max/sum need only one exchange with lane ^ 32.
+//  * P^T stays in registers and is the k-operand of O^T += V^T P^T; V^T fragments come from the
+//    row-major V tile through transposing LDS reads.
+//  * grid order: heaviest query tiles first (causal / document masks load late tiles most).
+#include "fm_common.h"
+
+namespace fm {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int* lts;
+  const int* lte;
+  const int* uts;
+  const int* ute;
+  const int* bounds;
+  int B, H, N, Hm;
+  int nq;   // query tiles per head
+  int nkb;  // bounds entries per (b, hm) row
+  int causal;
+  float scale_log2;  // scale * log2(e)
+};
+
+template <typename T, int D>
+struct FwdTraits {
+  static constexpr int BR = 128;
+  static constexpr int BC = 64;
+  static constexpr int NT = 256;
+  static constexpr int PITCH = D + 16 / (int)sizeof(T);  // 16-byte row padding
+  static constexpr int NQF = D / MM<T>::KW;              // Q fragments per lane
+  static constexpr int NDB = D / 32;                     // 32-wide output column blocks
+  static constexpr int TPB = 16 / MM<T>::E;              // products per 32-key block in P V
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+  using Tr = FwdTraits<T, D>;
+  using M = MM<T>;
+  constexpr int BR = Tr::BR, BC = Tr::BC, PITCH = Tr::PITCH;
+  __shared__ __attribute__((aligned(16))) T k_lds[BC * PITCH];
+  __shared__ __attribute__((aligned(16))) T v_lds[BC * PITCH];
+  __shared__ __attribute__((aligned(16))) int vec_lds[4][BC];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int qt = a.nq - 1 - (int)(blockIdx.x / BH);
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int hm = a.Hm > 1 ? h : 0;
+  const int N = a.N;
+  const int r0 = qt * BR;
+  const int r1 = min(N, r0 + BR);
+  const int row = r0 + wave * 32 + l32;  // this lane's query row
+
+  const size_t head = (size_t)bh * N * D;
+  const T* __restrict__ qg = static_cast<const T*>(a.q) + head;
+  const T* __restrict__ kg = static_cast<const T*>(a.k) + head;
+  const T* __restrict__ vg = static_cast<const T*>(a.v) + head;
+  const size_t vrow = ((size_t)b * a.Hm + hm) * N;
+  const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
+  const bool has_lt = a.lts != nullptr;
+  const bool has_ut = a.uts != nullptr;
+  const bool causal = a.causal != 0;
+
+  // Q^T operand: lane holds row `row`, k = d in chunks of KW.
+  typename M::frag qf[Tr::NQF];
+#pragma unroll
+  for (int c = 0; c < Tr::NQF; ++c) {
+    if (row < N) {
+      qf[c] = load_kcontig_frag<T>(qg + (size_t)row * D + c * M::KW + g * M::E);
+    } else {
+      qf[c] = typename M::frag{};
+    }
+  }
+
+  f32x16 o[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) o[db] = zero16();
+  float m_run = -INFINITY;  // running max of scale*log2e*score for this row
+  float l_run = 0.f;        // this lane's share of the running denominator
+
+  const int nkt = (N + BC - 1) / BC;
+  const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
+
+  for (int kt = 0; kt < kt_end; ++kt) {
+    const int c0 = kt * BC;
+    const int c1 = min(N, c0 + BC);
+    int bnd[8];
+    merged_bounds(brow, kt, kt + 1, N, bnd);
+    const int cls = classify_tile(r0, r1, c0, c1, bnd, causal);
+    if (cls == CLS_FULL) continue;
+    const bool need_mask = (cls == CLS_PARTIAL) || (c1 - c0 < BC);
+
+    __syncthreads();  // previous tile's LDS reads are done
+    load_tile<T, BC, D, PITCH, Tr::NT>(k_lds, kg, c0, N, tid);
+    load_tile<T, BC, D, PITCH, Tr::NT>(v_lds, vg, c0, N, tid);
+    if (need_mask && tid < BC) {
+      const int j = c0 + tid;
+      const bool ok = j < N;
+      vec_lds[0][tid] = (has_lt && ok) ? a.lts[vrow + j] : 0;
+      vec_lds[1][tid] = (has_lt && ok) ? a.lte[vrow + j] : 0;
+      vec_lds[2][tid] = (has_ut && ok) ? a.uts[vrow + j] : 0;
+      vec_lds[3][tid] = (has_ut && ok) ? a.ute[vrow + j] : 0;
+    }
+    __syncthreads();
+
+    // S^T for the two 32-key blocks: rows = keys, columns = this wave's queries.
+    f32x16 s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      s[jb] = zero16();
+      const T* krow = k_lds + (jb * 32 + l32) * PITCH + g * M::E;
+#pragma unroll
+      for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(load_kcontig_frag<T>(krow + c * M::KW), qf[c], s[jb]);
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[jb][r] * a.scale_log2;
+        if (need_mask) {
+          const int jl = jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const int j = c0 + jl;
+          const bool msk = (j >= N) || masked_elem(row, j, causal, has_lt, has_ut, vec_lds[0][jl], vec_lds[1][jl],
+                                                   vec_lds[2][jl], vec_lds[3][jl]);
+          x = msk ? -INFINITY : x;
+        }
+        s[jb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(s[jb][r] - m_use);
+        s[jb][r] = p;
+        psum += p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+
+    // O^T += V^T P^T over the 64 keys of the tile.
+#pragma unroll
+    for (int t = 0; t < 2 * Tr::TPB; ++t) {
+      const typename M::frag pf = acc_frag<T>(s[t / Tr::TPB], t % Tr::TPB);
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        const typename M::frag vf = load_kmajor_frag<T>(v_lds, PITCH, 0, db * 32, t, lane);
+        o[db] = M::mma(vf, pf, o[db]);
+      }
+    }
+  }
+
+  // Epilogue: out = O / l, lse = max * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (row < N) {
+    const bool dead = !(l_tot > 0.f);
+    const float inv = dead ? 0.f : 1.f / l_tot;
+    T* og = static_cast<T*>(a.out) + head + (size_t)row * D;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[db][4 * q4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(og + d0) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = o[db][4 * q4 + e] * inv;
+          *reinterpret_cast<f32x4*>(og + d0) = w;
+        }
+      }
+    }
+    if (g == 0) a.lse[(size_t)bh * N + row] = dead ? -INFINITY : m_run * LN2 + __logf(l_tot);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  const long grid = (long)a.nq * a.B * a.H;
+  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+int fwd_qblock() { return 128; }
+
+hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
+                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
+                      int N, int Hm, int causal, float scale, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+  a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
+  a.B = B; a.H = H; a.N = N; a.Hm = Hm;
+  a.nq = (N + 127) / 128;
+  a.nkb = (N + KBLOCK - 1) / KBLOCK;
+  a.causal = causal;
+  a.scale_log2 = scale * LOG2E;
+  if (bf16_in) return d == 64 ? launch_fwd_t<bf16, 64>(a, stream) : launch_fwd_t<bf16, 128>(a, stream);
+  return d == 64 ? launch_fwd_t<float, 64>(a, stream) : launch_fwd_t<float, 128>(a, stream);
+}
+
+}  // namespace fm

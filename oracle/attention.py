@@ -127,14 +127,26 @@ def fwd_bwd(q, k, v, do, vectors, causal, scale, Hm, heads=None, workers=None):
     return out, lse, dq, dk, dv, workers
 
 
+def _live_span(masked):
+    live = np.flatnonzero(~masked.all(axis=0))
+    if live.size == 0:
+        return 0, 0
+    return int(live[0]), int(live[-1]) + 1
+
+
 def rows_probe(q, k, v, do, vecs, causal, scale, rows):
-    """out, lse, D and dq of selected query rows of one head, each from its full row of scores."""
-    N = k.shape[0]
+    """out, lse, D and dq of selected query rows of one head, each from its full row of scores
+    (only the span of columns holding an unmasked entry is multiplied)."""
+    N, d = k.shape
     rows = np.asarray(rows, dtype=np.int64)
     outs, lses, Ds, dqs = [], [], [], []
     for i in rows:
         masked = dense_masked_rows(*vecs, causal, N, int(i), int(i) + 1)
-        res = attend_rows(q[i:i + 1], k, v, do[i:i + 1], masked, scale)
+        c0, c1 = _live_span(masked)
+        if c1 == c0:
+            outs.append(np.zeros(d)); lses.append(-np.inf); Ds.append(0.0); dqs.append(np.zeros(d))
+            continue
+        res = attend_rows(q[i:i + 1], k[c0:c1], v[c0:c1], do[i:i + 1], masked[:, c0:c1], scale)
         outs.append(res["out"][0])
         lses.append(res["lse"][0])
         Ds.append(res["D"][0])
@@ -163,9 +175,12 @@ def cols_probe(q, k, v, do, vecs, causal, scale, cols, row_block=64):
     for s in range(0, rows.size, row_block):
         rr = rows[s:s + row_block]
         masked = np.concatenate([dense_masked_rows(*vecs, causal, N, int(i), int(i) + 1) for i in rr])
-        res = attend_rows(q[rr], k, v, do[rr], masked, scale)
-        dk += scale * (res["dS"][:, cols].T @ q[rr])
-        dv += res["P"][:, cols].T @ do[rr]
+        c0, c1 = _live_span(masked)
+        res = attend_rows(q[rr], k[c0:c1], v[c0:c1], do[rr], masked[:, c0:c1], scale)
+        sel = (cols >= c0) & (cols < c1)
+        local = cols[sel] - c0
+        dk[sel] += scale * (res["dS"][:, local].T @ q[rr])
+        dv[sel] += res["P"][:, local].T @ do[rr]
     return dk, dv
 
 

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every symbol include/fm.h declares, and rejects bad arguments on
+the host before any launch (CPU: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mask_aware_exact_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fm.LIB_PATH):
+        fm_build = __import__("mask_aware_exact_amd.build", fromlist=["build"])
+        fm_build.build()
+    return fm.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(fm.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_size_queries(lib):
+    assert lib.fm_kblock() == 64
+    assert lib.fm_fwd_qblock(64) == 128 and lib.fm_fwd_qblock(128) == 128 and lib.fm_fwd_qblock(96) == 0
+    assert lib.fm_bounds_elems(1, 1, 1) == 8
+    assert lib.fm_bounds_elems(2, 3, 130) == 2 * 3 * 3 * 8
+    assert lib.fm_bounds_elems(0, 1, 10) == 0 and lib.fm_bounds_elems(1, 1, (1 << 24) + 1) == 0
+    n = lib.fm_bwd_workspace_bytes(fm.FM_BF16, 1, 2, 100, 64)
+    assert n >= 1 * 2 * 100 * 64 * 4 + 1 * 2 * 100 * 4 and n % 256 == 0
+    assert lib.fm_bwd_workspace_bytes(fm.FM_BF16, 1, 2, 100, 96) == 0
+    assert lib.fm_bwd_workspace_bytes(7, 1, 2, 100, 64) == 0
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert isinstance(fm.status_str(s), str) and fm.status_str(s)
+    assert fm.status_str(42) == "unknown status"
+
+
+P = ctypes.c_void_p
+A = P(0x100000)  # an aligned stand-in address: every call below is rejected before it is used
+B_ = P(0x200000)
+
+
+def _fwd(lib, **kw):
+    args = dict(q=A, k=A, v=A, dtype=fm.FM_BF16, B=1, H=2, N=100, d=64, lts=None, lte=None, uts=None,
+                ute=None, Hm=1, bounds=None, causal=1, scale=0.125, out=B_, lse=B_)
+    args.update(kw)
+    return lib.fm_fwd(args["q"], args["k"], args["v"], args["dtype"], args["B"], args["H"], args["N"],
+                      args["d"], args["lts"], args["lte"], args["uts"], args["ute"], args["Hm"], args["bounds"],
+                      args["causal"], args["scale"], args["out"], args["lse"], None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, q=None) == fm.FM_ERR_INVALID
+    assert _fwd(lib, out=None) == fm.FM_ERR_INVALID
+    assert _fwd(lib, lse=None) == fm.FM_ERR_INVALID
+    assert _fwd(lib, B=0) == fm.FM_ERR_INVALID
+    assert _fwd(lib, N=-5) == fm.FM_ERR_INVALID
+    assert _fwd(lib, N=(1 << 24) + 1) == fm.FM_ERR_INVALID
+    assert _fwd(lib, scale=float("inf")) == fm.FM_ERR_INVALID
+    assert _fwd(lib, scale=float("nan")) == fm.FM_ERR_INVALID
+    assert _fwd(lib, lts=A) == fm.FM_ERR_INVALID                      # half-NULL pair
+    assert _fwd(lib, ute=A) == fm.FM_ERR_INVALID
+    assert _fwd(lib, lts=A, lte=A) == fm.FM_ERR_INVALID               # vectors without bounds
+    assert _fwd(lib, lts=A, lte=A, bounds=A, Hm=3) == fm.FM_ERR_INVALID  # Hm not in {1, H}
+    assert _fwd(lib, d=96) == fm.FM_ERR_UNSUPPORTED
+    assert _fwd(lib, d=256) == fm.FM_ERR_UNSUPPORTED
+    assert _fwd(lib, dtype=5) == fm.FM_ERR_UNSUPPORTED
+    assert _fwd(lib, q=P(0x100002)) == fm.FM_ERR_INVALID              # misaligned
+
+
+def _bwd(lib, **kw):
+    args = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, dtype=fm.FM_BF16, B=1, H=2, N=100, d=64, lts=None,
+                lte=None, uts=None, ute=None, Hm=1, bounds=None, causal=1, scale=0.125, dq=B_, dk=B_, dv=B_,
+                ws=P(0x300000), ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.fm_bwd(args["q"], args["k"], args["v"], args["out"], args["dout"], args["lse"], args["dtype"],
+                      args["B"], args["H"], args["N"], args["d"], args["lts"], args["lte"], args["uts"],
+                      args["ute"], args["Hm"], args["bounds"], args["causal"], args["scale"], args["dq"],
+                      args["dk"], args["dv"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bwd_validation(lib):
+    for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"):
+        assert _bwd(lib, **{name: None}) == fm.FM_ERR_INVALID, name
+    assert _bwd(lib, H=0) == fm.FM_ERR_INVALID
+    assert _bwd(lib, uts=A) == fm.FM_ERR_INVALID
+    assert _bwd(lib, uts=A, ute=A) == fm.FM_ERR_INVALID
+    assert _bwd(lib, d=32) == fm.FM_ERR_UNSUPPORTED
+    assert _bwd(lib, ws=None) == fm.FM_ERR_WORKSPACE
+    need = lib.fm_bwd_workspace_bytes(fm.FM_BF16, 1, 2, 100, 64)
+    assert _bwd(lib, ws_bytes=need - 1) == fm.FM_ERR_WORKSPACE
+    assert _bwd(lib, dk=P(0x200008)) == fm.FM_ERR_INVALID
+
+
+def test_bounds_and_classes_validation(lib):
+    assert lib.fm_tile_bounds(A, A, None, None, 1, 1, 10, None, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_bounds(A, None, None, None, 1, 1, 10, B_, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_bounds(None, None, None, None, 0, 1, 10, B_, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_classes(A, 1, 1, 10, 1, 0, B_, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_classes(A, 1, 1, 10, 1, 64, None, None) == fm.FM_ERR_INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fm.fm_fwd(q, q, q)

@@ -1,0 +1,132 @@
+"""GPU parity of the HIP path (through the C ABI) with the fp64 oracle at sizes the oracle finishes in
+seconds: every mask family, both head dims, ragged tails, and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import tiles as OT
+from tests import fmcase as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mask_aware_exact_amd as m
+    m.load_library()
+    return m
+
+
+# (cfg, mask family, B, H, N, d, dtype)
+CASES = [
+    (0, "causal_document", 1, 2, 256, 64, "f32"),    # the tiny workload, exactly
+    (0, "causal_document", 1, 2, 256, 64, "bf16"),
+    (1, "full", 2, 3, 520, 64, "bf16"),
+    (1, "causal", 2, 3, 520, 64, "bf16"),
+    (2, "causal_document", 1, 4, 1000, 128, "bf16"),
+    (2, "causal_window_1024", 1, 3, 2600, 128, "bf16"),
+    (3, "share_question", 1, 3, 1500, 128, "bf16"),
+    (3, "prefix_lm", 1, 3, 1100, 128, "bf16"),
+    (3, "causal_key_drop", 1, 4, 1300, 128, "bf16"),
+    (4, "causal_document", 1, 2, 2500, 128, "bf16"),
+    (4, "causal_document_window_4096", 1, 2, 2500, 128, "bf16"),
+    (4, "causal_document_block_sparse", 1, 2, 2500, 128, "bf16"),
+    (3, "causal_key_drop", 2, 2, 777, 64, "bf16"),
+    (1, "bidirectional_document", 2, 2, 700, 64, "bf16"),
+    (1, "causal_by_vectors", 1, 2, 333, 128, "bf16"),
+    (2, "causal_document", 1, 2, 300, 128, "f32"),
+    (3, "prefix_lm", 1, 2, 200, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("cfg,mask,B,H,N,d,dtype", CASES, ids=lambda x: str(x))
+def test_parity_small(fm, cfg, mask, B, H, N, d, dtype):
+    case = C.make_case(cfg, mask, B, H, N, d, dtype)
+    print(f"\ncase {case.name}", flush=True)
+    gpu = C.run_gpu(case, fm)
+    ref = C.run_oracle(case)
+    report = {}
+    C.compare(gpu, ref, dtype, report)
+    print(report, flush=True)
+    if gpu["bounds"] is not None:
+        assert np.array_equal(gpu["bounds"].numpy(), C.oracle_bounds(case.spec))
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 129, 200])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tiny_and_ragged_sizes(fm, N, d):
+    case = C.make_case(2, "causal_document", 1, 2, N, d, "bf16") if N > 1 else \
+        C.make_case(1, "causal", 1, 2, N, d, "bf16")
+    print(f"\ncase {case.name}", flush=True)
+    C.compare(C.run_gpu(case, fm), C.run_oracle(case), "bf16")
+
+
+def test_every_key_dropped(fm):
+    # every column masked: every row is dead, every output and gradient is zero
+    N, H = 300, 2
+    spec = W.encode_causal_key_drop([np.arange(N)] * H, N)
+    case = C.make_case(3, "causal_key_drop", 1, H, N, 64, "bf16", spec=spec, name="all-dropped")
+    gpu = C.run_gpu(case, fm)
+    assert torch.all(gpu["out"] == 0) and torch.all(gpu["lse"] == -float("inf"))
+    for g in ("dq", "dk", "dv"):
+        assert torch.all(gpu[g] == 0)
+
+
+def test_dead_first_row(fm):
+    # dropping key 0 under causal leaves query 0 without keys
+    N, H = 400, 2
+    drops = [np.array([0, 5, 77, 399]), np.array([0])]
+    spec = W.encode_causal_key_drop(drops, N)
+    case = C.make_case(3, "causal_key_drop", 1, H, N, 128, "bf16", spec=spec, name="dead-row-0")
+    gpu = C.run_gpu(case, fm)
+    C.compare(gpu, C.run_oracle(case), "bf16")
+    assert torch.all(gpu["out"][0, :, 0] == 0) and torch.all(gpu["lse"][0, :, 0] == -float("inf"))
+
+
+def test_causal_flag_equals_vector_causal_bitwise(fm):
+    N, d = 700, 128
+    a = C.make_case(1, "causal", 1, 3, N, d, "bf16")
+    b = C.make_case(1, "causal", 1, 3, N, d, "bf16", spec=W.encode_causal_by_vectors(N))
+    ga, gb = C.run_gpu(a, fm), C.run_gpu(b, fm)
+    assert torch.equal(ga["out"], gb["out"]) and torch.equal(ga["lse"], gb["lse"])
+    assert torch.equal(ga["dk"], gb["dk"]) and torch.equal(ga["dv"], gb["dv"])
+    C.compare(gb, C.run_oracle(b), "bf16")
+
+
+def test_forward_is_deterministic(fm):
+    case = C.make_case(4, "causal_document", 1, 2, 1500, 128, "bf16")
+    a, b = C.run_gpu(case, fm), C.run_gpu(case, fm)
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["lse"], b["lse"])
+    assert torch.equal(a["dk"], b["dk"]) and torch.equal(a["dv"], b["dv"])
+
+
+@pytest.mark.parametrize("mask", ["causal_document", "share_question", "prefix_lm", "causal_key_drop",
+                                  "causal_document_block_sparse", "bidirectional_document", "causal",
+                                  "full", "causal_window_1024"])
+@pytest.mark.parametrize("N", [1, 100, 1000, 4099])
+def test_bounds_and_classes_bit_exact(fm, mask, N):
+    H = 3
+    cfg = {"causal_document_block_sparse": 4, "share_question": 3, "prefix_lm": 3,
+           "causal_key_drop": 3}.get(mask, 2)
+    if N < 8 and mask in ("share_question",):
+        pytest.skip("needs room for a question and answers")
+    spec = W.make_mask(cfg, mask, 2, H, N)
+    vecs = C.device_vectors(spec)
+    has = any(x is not None for x in vecs)
+    bounds = fm.fm_tile_bounds(*vecs, 2, spec.Hm, N) if has else None
+    ref_b = OT.tile_bounds(spec.vectors(), 2, spec.Hm, N)
+    if has:
+        assert np.array_equal(bounds.cpu().numpy(), ref_b)
+    for qblock in (fm.fm_fwd_qblock(128), 64, 100):
+        cls = fm.fm_tile_classes(bounds, 2, spec.Hm, N, spec.causal, qblock).cpu().numpy()
+        assert np.array_equal(cls, OT.tile_classes(ref_b, N, spec.causal, qblock))
+
+
+def test_api_errors_on_gpu(fm):
+    q = torch.zeros(1, 2, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fm.FmError) as e:
+        fm.fm_fwd(q, q, q)
+    assert e.value.status == fm.FM_ERR_UNSUPPORTED

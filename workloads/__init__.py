@@ -231,10 +231,10 @@ def make_mask(cfg: int, mask_name: str, B: int, H: int, N: int, mask_index: Opti
             lo, hi = (1024, 32768) if N >= 32768 else (max(1, N // 128), max(2, N // 4))
             bounds = loguniform_doc_boundaries(rng, N, lo, hi)
         elif cfg == 0:
-            bounds = doc_boundaries_from_cuts(uniform_cuts(rng, 2, 1, N - 1), N)
+            bounds = doc_boundaries_from_cuts(uniform_cuts(rng, min(2, N - 1), 1, N - 1), N)
         else:
             K = int(rng.integers(2, 13))
-            bounds = doc_boundaries_from_cuts(uniform_cuts(rng, K - 1, 1, N - 1), N)
+            bounds = doc_boundaries_from_cuts(uniform_cuts(rng, min(K - 1, N - 1), 1, N - 1), N)
         return encode_causal_document(bounds, N, B)
     if mask_name.startswith("causal_window_"):
         w = int(mask_name.rsplit("_", 1)[1])
@@ -263,7 +263,7 @@ def make_mask(cfg: int, mask_name: str, B: int, H: int, N: int, mask_index: Opti
         return encode_causal_key_drop(drops, N, B)
     if mask_name == "bidirectional_document":
         K = int(rng.integers(2, 6))
-        bounds = doc_boundaries_from_cuts(uniform_cuts(rng, K - 1, 1, N - 1), N)
+        bounds = doc_boundaries_from_cuts(uniform_cuts(rng, min(K - 1, N - 1), 1, N - 1), N)
         return encode_bidirectional_document(bounds, N, B)
     raise ValueError(f"unknown mask family {mask_name!r}")
 
