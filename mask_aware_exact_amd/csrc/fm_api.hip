@@ -4,7 +4,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/fm.h"
+#include "fm.h"
 #include "fm_common.h"
 
 namespace fm {

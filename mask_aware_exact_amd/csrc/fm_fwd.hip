@@ -6,10 +6,18 @@
 // papers.pytorch.kr 2410.01359).
 //
 // Work decomposition (a design for 64-wide waves and 32x32 matrix cores, not taken from the pages):
-//  * one workgroup = 4 waves = BR = 128 query rows of one (b, h); wave w owns rows 32 w .. 32 w + 31.
-//  * key tiles of BC = 64 columns (one bounds entry) are staged row-major in LDS.
-//  * each wave computes S^T = K Q^T (keys as the M axis, its 32 queries as the N axis), so that every
-//    lane holds one query row: the row max/sum need only one exchange with lane ^ 32.
+//  * one workgroup = 4 waves = BR = 128 query rows of one (b, h); wave w owns rows 32 w .. 32 w + 31;
+//    two workgroups share a compute unit (one wave per SIMD each) so that one wave's softmax overlaps
+//    the other's matrix products.
+//  * key tiles of BC = 64 columns (one bounds entry). The live (not fully masked) tiles are found 64 at
+//    a time with one wave-wide ballot; the next live tile is fetched from HBM into registers while the
+//    current one is computed, and K / V are double-buffered row-major in LDS.
+//  * each wave computes S^T = K Q^T (keys as the M axis, its 32 queries as the N axis), so every lane
+//    holds one query row and the row max needs one exchange with lane ^ 32; the row sum stays split
+//    across the two lanes until the epilogue.
+//  * exponentials use a per-row reference max that is only raised when a tile's max exceeds it by more
+//    than 2^8 (log2 units); O and the row sum always share that reference, so the result is exact and
+//    the accumulator rescale runs only when the reference moves.
 //  * P^T stays in registers and is the k-operand of O^T += V^T P^T; V^T fragments come from the
 //    row-major V tile through transposing LDS reads.
 //  * grid order: heaviest query tiles first (causal / document masks load late tiles most).
@@ -44,16 +52,55 @@ struct FwdTraits {
   static constexpr int NQF = D / MM<T>::KW;              // Q fragments per lane
   static constexpr int NDB = D / 32;                     // 32-wide output column blocks
   static constexpr int TPB = 16 / MM<T>::E;              // products per 32-key block in P V
+  static constexpr int CPR = D * (int)sizeof(T) / 16;    // 16-byte chunks per K / V row
+  static constexpr int CH = BC * CPR / NT;               // chunks per thread per K / V tile
 };
 
+constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: unnormalised probabilities stay below 256
+
+// Live-tile window: bit t of `live` / `partial` describes key tile base + t.
+struct TileWindow {
+  int base;
+  uint64_t live;
+  uint64_t partial;
+};
+
+__device__ __forceinline__ TileWindow scan_tiles(int base, int kt_end, const int* brow, int r0, int r1, int N,
+                                                 int BC, bool causal, int lane) {
+  TileWindow w;
+  w.base = base;
+  const int t = base + lane;
+  int cls = CLS_FULL;
+  if (t < kt_end) {
+    int b[8];
+    merged_bounds(brow, t, t + 1, N, b);
+    cls = classify_tile(r0, r1, t * BC, min(N, t * BC + BC), b, causal);
+  }
+  w.live = __ballot(cls != CLS_FULL);
+  w.partial = __ballot(cls == CLS_PARTIAL);
+  return w;
+}
+
+// Next live tile at or after `from`, refilling the window as needed; kt_end when none is left.
+__device__ __forceinline__ int next_live(TileWindow& w, int from, int kt_end, const int* brow, int r0, int r1,
+                                         int N, int BC, bool causal, int lane) {
+  while (from < kt_end) {
+    if (from >= w.base + 64) w = scan_tiles(from, kt_end, brow, r0, r1, N, BC, causal, lane);
+    const uint64_t rest = w.live >> (from - w.base);
+    if (rest != 0) return from + __builtin_ctzll(rest);
+    from = w.base + 64;
+  }
+  return kt_end;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<T, D>;
   using M = MM<T>;
-  constexpr int BR = Tr::BR, BC = Tr::BC, PITCH = Tr::PITCH;
-  __shared__ __attribute__((aligned(16))) T k_lds[BC * PITCH];
-  __shared__ __attribute__((aligned(16))) T v_lds[BC * PITCH];
-  __shared__ __attribute__((aligned(16))) int vec_lds[4][BC];
+  constexpr int BR = Tr::BR, BC = Tr::BC, PITCH = Tr::PITCH, CPR = Tr::CPR, CH = Tr::CH;
+  __shared__ __attribute__((aligned(16))) T k_lds[2][BC * PITCH];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][BC * PITCH];
+  __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -81,6 +128,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const bool has_lt = a.lts != nullptr;
   const bool has_ut = a.uts != nullptr;
   const bool causal = a.causal != 0;
+  const float sl2 = a.scale_log2;
 
   // Q^T operand: lane holds row `row`, k = d in chunks of KW.
   typename M::frag qf[Tr::NQF];
@@ -96,82 +144,131 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   f32x16 o[Tr::NDB];
 #pragma unroll
   for (int db = 0; db < Tr::NDB; ++db) o[db] = zero16();
-  float m_run = -INFINITY;  // running max of scale*log2e*score for this row
-  float l_run = 0.f;        // this lane's share of the running denominator
+  float m_ref = -INFINITY;  // reference max (log2 units) of this row's exponentials
+  float l_run = 0.f;        // this lane's share of the denominator, relative to m_ref
 
   const int nkt = (N + BC - 1) / BC;
   const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
 
-  for (int kt = 0; kt < kt_end; ++kt) {
+  // Prefetch registers for one K / V tile and its mask vectors.
+  i32x4 kr[CH], vr[CH];
+  i32x4 mr = {0, 0, 0, 0};
+  auto fetch = [&](int kt) {
     const int c0 = kt * BC;
-    const int c1 = min(N, c0 + BC);
-    int bnd[8];
-    merged_bounds(brow, kt, kt + 1, N, bnd);
-    const int cls = classify_tile(r0, r1, c0, c1, bnd, causal);
-    if (cls == CLS_FULL) continue;
-    const bool need_mask = (cls == CLS_PARTIAL) || (c1 - c0 < BC);
-
-    __syncthreads();  // previous tile's LDS reads are done
-    load_tile<T, BC, D, PITCH, Tr::NT>(k_lds, kg, c0, N, tid);
-    load_tile<T, BC, D, PITCH, Tr::NT>(v_lds, vg, c0, N, tid);
-    if (need_mask && tid < BC) {
-      const int j = c0 + tid;
-      const bool ok = j < N;
-      vec_lds[0][tid] = (has_lt && ok) ? a.lts[vrow + j] : 0;
-      vec_lds[1][tid] = (has_lt && ok) ? a.lte[vrow + j] : 0;
-      vec_lds[2][tid] = (has_ut && ok) ? a.uts[vrow + j] : 0;
-      vec_lds[3][tid] = (has_ut && ok) ? a.ute[vrow + j] : 0;
+#pragma unroll
+    for (int it = 0; it < CH; ++it) {
+      const int c = it * Tr::NT + tid;
+      const int r = c / CPR, cc = c % CPR;
+      kr[it] = i32x4{0, 0, 0, 0};
+      vr[it] = i32x4{0, 0, 0, 0};
+      if (c0 + r < N) {
+        kr[it] = ld16(reinterpret_cast<const char*>(kg + (size_t)(c0 + r) * D) + cc * 16);
+        vr[it] = ld16(reinterpret_cast<const char*>(vg + (size_t)(c0 + r) * D) + cc * 16);
+      }
     }
-    __syncthreads();
+    if (tid < BC) {
+      const int j = c0 + tid;
+      mr = i32x4{0, 0, 0, 0};
+      if (j < N) {
+        if (has_lt) { mr[0] = a.lts[vrow + j]; mr[1] = a.lte[vrow + j]; }
+        if (has_ut) { mr[2] = a.uts[vrow + j]; mr[3] = a.ute[vrow + j]; }
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < CH; ++it) {
+      const int c = it * Tr::NT + tid;
+      const int r = c / CPR, cc = c % CPR;
+      st16(reinterpret_cast<char*>(&k_lds[buf][r * PITCH]) + cc * 16, kr[it]);
+      st16(reinterpret_cast<char*>(&v_lds[buf][r * PITCH]) + cc * 16, vr[it]);
+    }
+    if (tid < BC) vec_lds[buf][tid] = mr;
+  };
 
+  TileWindow win;
+  win.base = -64;
+  win.live = 0;
+  win.partial = 0;
+  int kt = next_live(win, 0, kt_end, brow, r0, r1, N, BC, causal, lane);
+  if (kt < kt_end) fetch(kt);
+  int buf = 0;
+
+  while (kt < kt_end) {
+    const int c0 = kt * BC;
+    const bool need_mask = ((win.partial >> (kt - win.base)) & 1) || (c0 + BC > N);
+    stash(buf);
+    __syncthreads();
+    const int kt_next = next_live(win, kt + 1, kt_end, brow, r0, r1, N, BC, causal, lane);
+    if (kt_next < kt_end) fetch(kt_next);
+
+    const T* kt_lds = k_lds[buf];
+    const T* vt_lds = v_lds[buf];
     // S^T for the two 32-key blocks: rows = keys, columns = this wave's queries.
     f32x16 s[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       s[jb] = zero16();
-      const T* krow = k_lds + (jb * 32 + l32) * PITCH + g * M::E;
+      const T* krow = kt_lds + (jb * 32 + l32) * PITCH + g * M::E;
 #pragma unroll
       for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(load_kcontig_frag<T>(krow + c * M::KW), qf[c], s[jb]);
     }
 
     float mx = -INFINITY;
+    if (need_mask) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+      for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[jb][r] * a.scale_log2;
-        if (need_mask) {
-          const int jl = jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const int j = c0 + jl;
-          const bool msk = (j >= N) || masked_elem(row, j, causal, has_lt, has_ut, vec_lds[0][jl], vec_lds[1][jl],
-                                                   vec_lds[2][jl], vec_lds[3][jl]);
-          x = msk ? -INFINITY : x;
+        for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jl = jb * 32 + 8 * q4 + 4 * g + e;
+            const int j = c0 + jl;
+            const i32x4 mv = vec_lds[buf][jl];
+            const bool msk = (j >= N) || masked_elem(row, j, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
+            const float x = msk ? -INFINITY : s[jb][4 * q4 + e] * sl2;
+            s[jb][4 * q4 + e] = x;
+            mx = fmaxf(mx, x);
+          }
         }
-        s[jb][r] = x;
-        mx = fmaxf(mx, x);
+      }
+    } else {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = s[jb][r] * sl2;
+          s[jb][r] = x;
+          mx = fmaxf(mx, x);
+        }
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // Raise the reference only when some row of the wave would exceed it by more than the threshold.
+    const bool grow = mx > m_ref + RESCALE_THRESHOLD;
+    if (__ballot(grow) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     float psum = 0.f;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[jb][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(s[jb][r] - m_use);
         s[jb][r] = p;
         psum += p;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
+    l_run += psum;
 
     // O^T += V^T P^T over the 64 keys of the tile.
 #pragma unroll
@@ -179,13 +276,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       const typename M::frag pf = acc_frag<T>(s[t / Tr::TPB], t % Tr::TPB);
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
-        const typename M::frag vf = load_kmajor_frag<T>(v_lds, PITCH, 0, db * 32, t, lane);
+        const typename M::frag vf = load_kmajor_frag<T>(vt_lds, PITCH, 0, db * 32, t, lane);
         o[db] = M::mma(vf, pf, o[db]);
       }
     }
+    kt = kt_next;
+    buf ^= 1;
   }
 
-  // Epilogue: out = O / l, lse = max * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
+  // Epilogue: out = O / l, lse = m_ref * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (row < N) {
     const bool dead = !(l_tot > 0.f);
@@ -209,7 +308,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (g == 0) a.lse[(size_t)bh * N + row] = dead ? -INFINITY : m_run * LN2 + __logf(l_tot);
+    if (g == 0) a.lse[(size_t)bh * N + row] = dead ? -INFINITY : m_ref * LN2 + logf(l_tot);
   }
 }
 
