@@ -5,14 +5,17 @@
 // 2410.01359). Three kernels run in order on the caller's stream:
 //  1. bwd_pre:  D_i = sum_d dO_id out_id (float32) per row, and the float32 dq accumulator cleared.
 //  2. bwd_main: one workgroup per (b, h, key tile of BC = 128 columns); wave w owns keys 32 w .. 32 w+31
-//     (one key column per lane). Per query tile of BR rows that the mask does not cover completely:
+//     (one key column per lane). The live query tiles (not fully masked for this key tile) are found
+//     64 at a time with a wave ballot; the next one is loaded into registers while the current one is
+//     computed, and Q / dO are double-buffered row-major in LDS. Per live query tile of BR rows:
 //       S = Q K^T and dP = dO V^T with K, V held in registers (keys as the N axis, so every lane keeps
 //       one key column and its four mask values in registers);
 //       P = exp(S - lse) (0 where masked), dS = P o (dP - D);
 //       dV^T += dO^T P and dK^T += Q^T dS, the k axis (query rows) read from the row-major Q / dO
 //       tiles through transposing LDS reads, accumulated on chip for the whole query loop;
-//       dS goes to LDS, and dQ_tile = dS K over the workgroup's 128 keys is added into the float32
-//       accumulator with hardware float atomics.
+//       dS goes to LDS, and each wave forms dQ = dS K for one 32-wide d block over the workgroup's
+//       128 keys, with that block of K held in registers (loaded once), and adds it into the float32
+//       accumulator with hardware float atomics (one 128-byte row segment per instruction).
 //  3. bwd_dq:   dq = accumulator rounded to the input type.
 #include "fm_common.h"
 
@@ -79,24 +82,30 @@ struct BwdTraits {
   static constexpr int NT = 256;
   static constexpr int PITCH = D + 16 / (int)sizeof(T);  // row-major Q / dO / K tiles
   static constexpr int PS = BR + 16 / (int)sizeof(T);    // dS tile [key][row]
-  static constexpr int NKF = D / MM<T>::KW;              // K / V fragments per lane
+  static constexpr int NKF = D / MM<T>::KW;              // K / V fragments per lane (k = d)
   static constexpr int NIB = BR / 32;                    // 32-row blocks per query tile
   static constexpr int NDB = D / 32;                     // 32-wide d blocks
   static constexpr int TPB = 16 / MM<T>::E;              // products per 32 k values
-  static constexpr int NQB = NIB * NDB;                  // dQ output blocks per query tile
+  static constexpr int NKQ = BC / 32 * TPB;              // products over the workgroup's keys (dQ)
+  static constexpr int WPD = 4 / NDB;                    // waves sharing one d block in dQ
+  static constexpr int CPR = D * (int)sizeof(T) / 16;    // 16-byte chunks per row
+  static constexpr int CH = BR * CPR / NT;               // chunks per thread per Q / dO tile
+  static_assert(BC * CPR % NT == 0 && CH >= 1, "tile copies must divide evenly");
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
   using Tr = BwdTraits<T, D>;
   using M = MM<T>;
-  constexpr int BC = Tr::BC, BR = Tr::BR, PITCH = Tr::PITCH, PS = Tr::PS;
-  __shared__ __attribute__((aligned(16))) T k_lds[BC * PITCH];
-  __shared__ __attribute__((aligned(16))) T q_lds[BR * PITCH];
-  __shared__ __attribute__((aligned(16))) T do_lds[BR * PITCH];
+  constexpr int BC = Tr::BC, BR = Tr::BR, PITCH = Tr::PITCH, PS = Tr::PS, CPR = Tr::CPR, CH = Tr::CH;
+  // q_lds / do_lds hold two query tiles each (double buffer); at start-up the same memory holds the K tile.
+  static_assert(4 * BR >= BC, "the K tile is staged through the query-tile buffers");
+  __shared__ __attribute__((aligned(16))) T qdo_lds[4 * BR * PITCH];
+  T* const q_lds = qdo_lds;
+  T* const do_lds = qdo_lds + 2 * BR * PITCH;
   __shared__ __attribute__((aligned(16))) T ds_lds[BC * PS];
-  __shared__ __attribute__((aligned(16))) float lse_lds[BR];
-  __shared__ __attribute__((aligned(16))) float dd_lds[BR];
+  __shared__ __attribute__((aligned(16))) float lse_lds[2][BR];
+  __shared__ __attribute__((aligned(16))) float dd_lds[2][BR];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -129,8 +138,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   const bool has_lt = a.lts != nullptr;
   const bool has_ut = a.uts != nullptr;
   const bool causal = a.causal != 0;
+  const float sl2 = a.scale_log2;
 
-  // This lane's key column: mask values and K / V fragments (k = d).
+  // This lane's key column: mask values and K / V fragments with k = d (operand B of S and dP).
   int m_lts = 0, m_lte = 0, m_uts = 0, m_ute = 0;
   typename M::frag kf[Tr::NKF], vf[Tr::NKF];
   if (j < N) {
@@ -148,7 +158,16 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       vf[c] = typename M::frag{};
     }
   }
-  load_tile<T, BC, D, PITCH, Tr::NT>(k_lds, kg, c0, N, tid);
+
+  // K fragments with k = key (operand B of dQ = dS K) for this wave's 32-wide d block, read once
+  // through the LDS from the row-major K tile.
+  const int wd = wave % Tr::NDB;
+  load_tile<T, BC, D, PITCH, Tr::NT>(q_lds, kg, c0, N, tid);
+  __syncthreads();
+  typename M::frag kq[Tr::NKQ];
+#pragma unroll
+  for (int t = 0; t < Tr::NKQ; ++t) kq[t] = load_kmajor_frag<T>(q_lds, PITCH, 0, wd * 32, t, lane);
+  __syncthreads();
 
   f32x16 dk[Tr::NDB], dv[Tr::NDB];
 #pragma unroll
@@ -161,35 +180,71 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N, bnd);
   const int nq = (N + BR - 1) / BR;
   const int qt_begin = causal ? c0 / BR : 0;
+  auto class_of = [&](int qt) { return classify_tile(qt * BR, min(N, qt * BR + BR), c0, c1, bnd, causal); };
 
-  for (int qt = qt_begin; qt < nq; ++qt) {
+  // Prefetch registers for one query tile.
+  i32x4 qr[CH], dr[CH];
+  float lr = 0.f, ddr = 0.f;
+  auto fetch = [&](int qt) {
     const int q0 = qt * BR;
-    const int q1 = min(N, q0 + BR);
-    const int cls = classify_tile(q0, q1, c0, c1, bnd, causal);
-    if (cls == CLS_FULL) continue;
-    const bool need_mask = (cls == CLS_PARTIAL) || (q1 - q0 < BR) || (c1 - c0 < BC);
-
-    __syncthreads();  // previous iteration's LDS reads are done
-    load_tile<T, BR, D, PITCH, Tr::NT>(q_lds, qg, q0, N, tid);
-    load_tile<T, BR, D, PITCH, Tr::NT>(do_lds, dog, q0, N, tid);
+#pragma unroll
+    for (int it = 0; it < CH; ++it) {
+      const int c = it * Tr::NT + tid;
+      const int r = c / CPR, cc = c % CPR;
+      qr[it] = i32x4{0, 0, 0, 0};
+      dr[it] = i32x4{0, 0, 0, 0};
+      if (q0 + r < N) {
+        qr[it] = ld16(reinterpret_cast<const char*>(qg + (size_t)(q0 + r) * D) + cc * 16);
+        dr[it] = ld16(reinterpret_cast<const char*>(dog + (size_t)(q0 + r) * D) + cc * 16);
+      }
+    }
     if (tid < BR) {
       const int i = q0 + tid;
-      float l = i < N ? lseg[i] : INFINITY;
-      // a row without any unmasked key has lse = -inf; +inf makes exp(S - lse) = 0 for it
-      l = (l == -INFINITY) ? INFINITY : l;
-      lse_lds[tid] = l * LOG2E;
-      dd_lds[tid] = i < N ? ddg[i] : 0.f;
+      lr = i < N ? lseg[i] : INFINITY;
+      ddr = i < N ? ddg[i] : 0.f;
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
+    T* qb = q_lds + buf * BR * PITCH;
+    T* db_ = do_lds + buf * BR * PITCH;
+#pragma unroll
+    for (int it = 0; it < CH; ++it) {
+      const int c = it * Tr::NT + tid;
+      const int r = c / CPR, cc = c % CPR;
+      st16(reinterpret_cast<char*>(qb + r * PITCH) + cc * 16, qr[it]);
+      st16(reinterpret_cast<char*>(db_ + r * PITCH) + cc * 16, dr[it]);
+    }
+    if (tid < BR) {
+      // a row without any unmasked key has lse = -inf; +inf makes exp(S - lse) = 0 for it
+      const float l = (lr == -INFINITY) ? INFINITY : lr;
+      lse_lds[buf][tid] = l * LOG2E;
+      dd_lds[buf][tid] = ddr;
+    }
+  };
 
+  TileWindow win = empty_window();
+  int qt = next_live_tile(win, qt_begin, nq, class_of, lane);
+  if (qt < nq) fetch(qt);
+  int buf = 0;
+
+  while (qt < nq) {
+    const int q0 = qt * BR;
+    const bool need_mask = window_partial(win, qt) || (q0 + BR > N) || (c0 + BC > N);
+    stash(buf);
+    __syncthreads();  // (A) this tile is in LDS; every wave is past the previous tile's dQ phase
+    const int qt_next = next_live_tile(win, qt + 1, nq, class_of, lane);
+    if (qt_next < nq) fetch(qt_next);
+
+    const T* qb = q_lds + buf * BR * PITCH;
+    const T* dob = do_lds + buf * BR * PITCH;
     // S = Q K^T and dP = dO V^T: rows = this tile's queries, columns = this wave's keys.
     f32x16 s[Tr::NIB], dp[Tr::NIB];
 #pragma unroll
     for (int ib = 0; ib < Tr::NIB; ++ib) {
       s[ib] = zero16();
       dp[ib] = zero16();
-      const T* qrow = q_lds + (ib * 32 + l32) * PITCH + g * M::E;
-      const T* dorow = do_lds + (ib * 32 + l32) * PITCH + g * M::E;
+      const T* qrow = qb + (ib * 32 + l32) * PITCH + g * M::E;
+      const T* dorow = dob + (ib * 32 + l32) * PITCH + g * M::E;
 #pragma unroll
       for (int c = 0; c < Tr::NKF; ++c) {
         s[ib] = M::mma(load_kcontig_frag<T>(qrow + c * M::KW), kf[c], s[ib]);
@@ -203,12 +258,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int il0 = ib * 32 + 8 * q4 + 4 * g;
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_lds + il0);
-        const f32x4 dd4 = *reinterpret_cast<const f32x4*>(dd_lds + il0);
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
+        const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[buf][il0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q4 + e;
-          float p = exp2f(s[ib][r] * a.scale_log2 - lse4[e]);
+          float p = __builtin_amdgcn_exp2f(s[ib][r] * sl2 - lse4[e]);
           if (need_mask) {
             const int i = q0 + il0 + e;
             const bool msk = (i >= N) || (j >= N) ||
@@ -228,8 +283,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       const typename M::frag sf = acc_frag<T>(dp[t / Tr::TPB], t % Tr::TPB);
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
-        dv[db] = M::mma(load_kmajor_frag<T>(do_lds, PITCH, 0, db * 32, t, lane), pf, dv[db]);
-        dk[db] = M::mma(load_kmajor_frag<T>(q_lds, PITCH, 0, db * 32, t, lane), sf, dk[db]);
+        dv[db] = M::mma(load_kmajor_frag<T>(dob, PITCH, 0, db * 32, t, lane), pf, dv[db]);
+        dk[db] = M::mma(load_kmajor_frag<T>(qb, PITCH, 0, db * 32, t, lane), sf, dk[db]);
       }
     }
 
@@ -253,26 +308,23 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // (B) dS of all four waves is in LDS
 
-    // dQ tile += scale * dS K over the workgroup's keys; each wave owns some (row block, d block) pairs.
-    for (int ob = wave; ob < Tr::NQB; ob += 4) {
-      const int ib = ob / Tr::NDB;
-      const int db = ob % Tr::NDB;
+    // dQ rows += scale * dS K over the workgroup's keys, for this wave's d block.
+#pragma unroll
+    for (int ib = wave / Tr::NDB; ib < Tr::NIB; ib += Tr::WPD) {
       f32x16 acc = zero16();
 #pragma unroll
-      for (int t = 0; t < BC / 32 * Tr::TPB; ++t) {
-        const typename M::frag af = load_kmajor_frag<T>(ds_lds, PS, 0, ib * 32, t, lane);
-        const typename M::frag bfr = load_kmajor_frag<T>(k_lds, PITCH, 0, db * 32, t, lane);
-        acc = M::mma(af, bfr, acc);
-      }
-      const int d = db * 32 + l32;
+      for (int t = 0; t < Tr::NKQ; ++t) acc = M::mma(load_kmajor_frag<T>(ds_lds, PS, 0, ib * 32, t, lane), kq[t], acc);
+      const int d = wd * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = q0 + ib * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         if (i < N) unsafeAtomicAdd(dqg + (size_t)i * D + d, acc[r] * a.scale);
       }
     }
+    qt = qt_next;
+    buf ^= 1;
   }
 
   // dK = scale * dK^T, dV = dV^T for this lane's key column.

@@ -63,6 +63,47 @@ __device__ inline void merged_bounds(const int* __restrict__ brow, int kt0, int 
   }
 }
 
+// Live-tile window over 64 consecutive tiles: bit t of `live` / `partial` describes tile base + t.
+// One wave-wide ballot classifies 64 tiles at once; every wave of a workgroup computes the same window.
+struct TileWindow {
+  int base;
+  uint64_t live;
+  uint64_t partial;
+};
+
+template <typename ClassOf>
+__device__ __forceinline__ TileWindow scan_window(int base, int end, ClassOf class_of, int lane) {
+  TileWindow w;
+  w.base = base;
+  const int t = base + lane;
+  const int cls = t < end ? class_of(t) : (int)CLS_FULL;
+  w.live = __ballot(cls != CLS_FULL);
+  w.partial = __ballot(cls == CLS_PARTIAL);
+  return w;
+}
+
+// Next live tile at or after `from` (refilling the window as needed), or `end` when none is left.
+template <typename ClassOf>
+__device__ __forceinline__ int next_live_tile(TileWindow& w, int from, int end, ClassOf class_of, int lane) {
+  while (from < end) {
+    if (from >= w.base + 64) w = scan_window(from, end, class_of, lane);
+    const uint64_t rest = w.live >> (from - w.base);
+    if (rest != 0) return from + __builtin_ctzll(rest);
+    from = w.base + 64;
+  }
+  return end;
+}
+
+__device__ __forceinline__ TileWindow empty_window() {
+  TileWindow w;
+  w.base = -64;
+  w.live = 0;
+  w.partial = 0;
+  return w;
+}
+
+__device__ __forceinline__ bool window_partial(const TileWindow& w, int t) { return (w.partial >> (t - w.base)) & 1; }
+
 // Whether query row i is masked for a key column with the given vector values.
 __device__ __forceinline__ bool masked_elem(int i, int j, bool causal, bool has_lt, bool has_ut, int lts,
                                             int lte, int uts, int ute) {

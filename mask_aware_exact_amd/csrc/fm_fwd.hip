@@ -58,41 +58,6 @@ struct FwdTraits {
 
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: unnormalised probabilities stay below 256
 
-// Live-tile window: bit t of `live` / `partial` describes key tile base + t.
-struct TileWindow {
-  int base;
-  uint64_t live;
-  uint64_t partial;
-};
-
-__device__ __forceinline__ TileWindow scan_tiles(int base, int kt_end, const int* brow, int r0, int r1, int N,
-                                                 int BC, bool causal, int lane) {
-  TileWindow w;
-  w.base = base;
-  const int t = base + lane;
-  int cls = CLS_FULL;
-  if (t < kt_end) {
-    int b[8];
-    merged_bounds(brow, t, t + 1, N, b);
-    cls = classify_tile(r0, r1, t * BC, min(N, t * BC + BC), b, causal);
-  }
-  w.live = __ballot(cls != CLS_FULL);
-  w.partial = __ballot(cls == CLS_PARTIAL);
-  return w;
-}
-
-// Next live tile at or after `from`, refilling the window as needed; kt_end when none is left.
-__device__ __forceinline__ int next_live(TileWindow& w, int from, int kt_end, const int* brow, int r0, int r1,
-                                         int N, int BC, bool causal, int lane) {
-  while (from < kt_end) {
-    if (from >= w.base + 64) w = scan_tiles(from, kt_end, brow, r0, r1, N, BC, causal, lane);
-    const uint64_t rest = w.live >> (from - w.base);
-    if (rest != 0) return from + __builtin_ctzll(rest);
-    from = w.base + 64;
-  }
-  return kt_end;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<T, D>;
@@ -186,20 +151,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if (tid < BC) vec_lds[buf][tid] = mr;
   };
 
-  TileWindow win;
-  win.base = -64;
-  win.live = 0;
-  win.partial = 0;
-  int kt = next_live(win, 0, kt_end, brow, r0, r1, N, BC, causal, lane);
+  auto class_of = [&](int t) {
+    int bt[8];
+    merged_bounds(brow, t, t + 1, N, bt);
+    return classify_tile(r0, r1, t * BC, min(N, t * BC + BC), bt, causal);
+  };
+  TileWindow win = empty_window();
+  int kt = next_live_tile(win, 0, kt_end, class_of, lane);
   if (kt < kt_end) fetch(kt);
   int buf = 0;
 
   while (kt < kt_end) {
     const int c0 = kt * BC;
-    const bool need_mask = ((win.partial >> (kt - win.base)) & 1) || (c0 + BC > N);
+    const bool need_mask = window_partial(win, kt) || (c0 + BC > N);
     stash(buf);
     __syncthreads();
-    const int kt_next = next_live(win, kt + 1, kt_end, brow, r0, r1, N, BC, causal, lane);
+    const int kt_next = next_live_tile(win, kt + 1, kt_end, class_of, lane);
     if (kt_next < kt_end) fetch(kt_next);
 
     const T* kt_lds = k_lds[buf];
