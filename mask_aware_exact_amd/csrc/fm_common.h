@@ -104,13 +104,30 @@ __device__ __forceinline__ TileWindow empty_window() {
 
 __device__ __forceinline__ bool window_partial(const TileWindow& w, int t) { return (w.partial >> (t - w.base)) & 1; }
 
-// Whether query row i is masked for a key column with the given vector values.
+// Whether query row i is masked for a key column with the given vector values. Bitwise operators
+// only, so that the compiler emits selects rather than branches.
 __device__ __forceinline__ bool masked_elem(int i, int j, bool causal, bool has_lt, bool has_ut, int lts,
                                             int lte, int uts, int ute) {
-  bool m = causal && (i < j);
-  m |= has_lt && (lts <= i) && (i < lte);
-  m |= has_ut && (uts <= i) && (i < ute);
-  return m;
+  return (causal & (i < j)) | (has_lt & (lts <= i) & (i < lte)) | (has_ut & (uts <= i) & (i < ute));
+}
+
+// Bits of the query rows [s, e) that fall in [q0, q0 + 64), bit k standing for row q0 + k.
+__device__ __forceinline__ uint64_t row_span_bits(int s, int e, int q0) {
+  const int a = max(s - q0, 0);
+  const int z = min(e - q0, 64);
+  const uint64_t below_z = z >= 64 ? ~0ull : (z <= 0 ? 0ull : (1ull << z) - 1);
+  const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1;
+  return below_z & ~below_a;
+}
+
+// Masked rows among q0 .. q0 + 63 for key column j (rows and columns at or past N count as masked).
+__device__ __forceinline__ uint64_t masked_row_bits(int q0, int j, int N, bool causal, bool has_lt, bool has_ut,
+                                                    int lts, int lte, int uts, int ute) {
+  uint64_t m = row_span_bits(N, 0x7fffffff, q0);
+  m |= causal ? row_span_bits(0, j, q0) : 0ull;
+  m |= has_lt ? row_span_bits(lts, lte, q0) : 0ull;
+  m |= has_ut ? row_span_bits(uts, ute, q0) : 0ull;
+  return j >= N ? ~0ull : m;
 }
 
 // ------------------------------------------------------------------ matrix-core traits
@@ -198,6 +215,47 @@ __device__ __forceinline__ bf16x8 acc_frag<bf16>(const f32x16& acc, int t) {
 template <>
 __device__ __forceinline__ float acc_frag<float>(const f32x16& acc, int t) {
   return acc[t];
+}
+
+// ------------------------------------------------------------------ swizzled bf16 tiles
+// A bf16 tile with rows of D elements (D * 2 bytes, unpadded) stores 16-byte chunk c of row r at chunk
+// position c ^ swz_key<D>(r). With 64 LDS banks of 4 bytes this makes both access patterns of the kernels
+// conflict-free: 16 lanes reading the same chunk of 16 consecutive rows (operand fragments with k along
+// the row), and 32 lanes reading 64 bytes of 4 consecutive rows (transposing reads, k along the rows).
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  static_assert(D == 64 || D == 128, "swizzled tiles are defined for 64 and 128 columns");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset of element `col` (a multiple of 4) of row r in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * (D * 2) + (((col >> 3) ^ swz_key<D>(r)) << 4) + ((col & 7) << 1);
+}
+
+// 8 consecutive elements (k contiguous along the row) from a swizzled tile: col is a multiple of 8.
+template <int D>
+__device__ __forceinline__ bf16x8 swz_kcontig(const bf16* tile, int r, int col) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + swz_off<D>(r, col));
+}
+
+// load_kmajor_frag for a swizzled tile (see load_kmajor_frag for the k order).
+template <int D>
+__device__ __forceinline__ bf16x8 swz_kmajor(const bf16* tile, int row0, int col0, int t, int lane) {
+  const int g = lane >> 5;
+  const int s = lane & 15;
+  const int col = col0 + (lane & 16) + 4 * (s & 3);
+  const int row = row0 + 16 * t + 4 * g + (s >> 2);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const char* base = reinterpret_cast<const char*>(tile);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + swz_off<D>(row, col)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + swz_off<D>(row + 8, col)));
+  bf16x8 f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
 }
 
 // 16-byte global/LDS copy helpers.

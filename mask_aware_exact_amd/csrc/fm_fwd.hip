@@ -11,7 +11,9 @@
 //    the other's matrix products.
 //  * key tiles of BC = 64 columns (one bounds entry). The live (not fully masked) tiles are found 64 at
 //    a time with one wave-wide ballot; the next live tile is fetched from HBM into registers while the
-//    current one is computed, and K / V are double-buffered row-major in LDS.
+//    current one is computed, and K / V are double-buffered in LDS. K rows are padded by 16 bytes
+//    (32 lanes reading one 16-byte chunk of 32 rows hit distinct banks); V rows by 64 bytes (the four
+//    rows of one transposing read start 16 banks apart).
 //  * each wave computes S^T = K Q^T (keys as the M axis, its 32 queries as the N axis), so every lane
 //    holds one query row and the row max needs one exchange with lane ^ 32; the row sum stays split
 //    across the two lanes until the epilogue.
@@ -48,7 +50,9 @@ struct FwdTraits {
   static constexpr int BR = 128;
   static constexpr int BC = 64;
   static constexpr int NT = 256;
-  static constexpr int PITCH = D + 16 / (int)sizeof(T);  // 16-byte row padding
+  static constexpr int PITCH = D + 16 / (int)sizeof(T);  // K rows: 16-byte padding (row-wise reads)
+  // V rows (bf16): 64-byte padding, so that the four rows of one transposing read start 16 banks apart
+  static constexpr int VPITCH = sizeof(T) == 2 ? D + 32 : PITCH;
   static constexpr int NQF = D / MM<T>::KW;              // Q fragments per lane
   static constexpr int NDB = D / 32;                     // 32-wide output column blocks
   static constexpr int TPB = 16 / MM<T>::E;              // products per 32-key block in P V
@@ -63,8 +67,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<T, D>;
   using M = MM<T>;
   constexpr int BR = Tr::BR, BC = Tr::BC, PITCH = Tr::PITCH, CPR = Tr::CPR, CH = Tr::CH;
+  constexpr int VPITCH = Tr::VPITCH;
   __shared__ __attribute__((aligned(16))) T k_lds[2][BC * PITCH];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][BC * PITCH];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VPITCH];
   __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
 
   const int tid = threadIdx.x;
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       const int c = it * Tr::NT + tid;
       const int r = c / CPR, cc = c % CPR;
       st16(reinterpret_cast<char*>(&k_lds[buf][r * PITCH]) + cc * 16, kr[it]);
-      st16(reinterpret_cast<char*>(&v_lds[buf][r * PITCH]) + cc * 16, vr[it]);
+      st16(reinterpret_cast<char*>(&v_lds[buf][r * VPITCH]) + cc * 16, vr[it]);
     }
     if (tid < BC) vec_lds[buf][tid] = mr;
   };
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const int jl = jb * 32 + 8 * q4 + 4 * g + e;
             const int j = c0 + jl;
             const i32x4 mv = vec_lds[buf][jl];
-            const bool msk = (j >= N) || masked_elem(row, j, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
+            const bool msk = (j >= N) | masked_elem(row, j, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
             const float x = msk ? -INFINITY : s[jb][4 * q4 + e] * sl2;
             s[jb][4 * q4 + e] = x;
             mx = fmaxf(mx, x);
@@ -243,8 +248,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       const typename M::frag pf = acc_frag<T>(s[t / Tr::TPB], t % Tr::TPB);
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
-        const typename M::frag vf = load_kmajor_frag<T>(vt_lds, PITCH, 0, db * 32, t, lane);
-        o[db] = M::mma(vf, pf, o[db]);
+        o[db] = M::mma(load_kmajor_frag<T>(vt_lds, VPITCH, 0, db * 32, t, lane), pf, o[db]);
       }
     }
     kt = kt_next;
