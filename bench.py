@@ -4,10 +4,13 @@ A step is one pass of the whole path over one batch of synthetic input:
 fm_tile_bounds -> fm_fwd -> fm_bwd. The metric counts only unmasked FLOPs:
     FLOP per step = 14 * d * U   (forward 4 d U: Q K^T and P V; backward 10 d U: the S recompute,
                                   dP, dV, dK and dQ products), U = unmasked (query, key) pairs.
-The default workload is SFT packing with a causal document mask (B=1, H=32, N=8192, d=128, bf16).
+The default workload is the long-context configuration with a causal document mask (B=1, H=8,
+N=131072, d=128, bf16; document lengths log-uniform in [1K, 32K]), the largest head-dim-128 workload.
 
 Prints one JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --no-cpu-baseline,
---sweep (also time the other head-dim-128 workloads, a few steps each, reported under "sweep").
+--sweep (also time the other head-dim-128 workloads, a few steps each, reported under "sweep"),
+--copy-calibration (after timing, one 1 GiB device-to-device copy, the reference kernel for scaling
+hardware byte counters in profiling runs).
 """
 from __future__ import annotations
 
@@ -42,7 +45,37 @@ WORKLOADS = {
     "bert_base_full": (1, "full"),
     "bert_base_causal": (1, "causal"),
 }
-DEFAULT_WORKLOAD = "sft_packing_causal_document"
+DEFAULT_WORKLOAD = "long_context_causal_document"
+ROOFLINE_KERNEL = "fm_bwd"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fm_bwd_long_context_causal_document_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "mask_aware_exact_amd", "csrc", f)
+                  for f in ("fm_common.h", "fm_bwd.hip")]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per fm_bwd call from the committed counter summary, or None when that summary is
+    missing, covers another workload, or was taken from other kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and line.startswith("- "):
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("workload") != workload or fields.get("kernel_source_digest") != kernel_source_digest():
+            return None
+        return int(float(fields["hbm_bytes_per_call"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def unmasked_pairs(spec: W.MaskSpec, H: int) -> int:
@@ -143,26 +176,30 @@ def time_workload(fm, wl: Workload, steps: int, warmup: int):
     return wall, parts.mean(axis=0), ok
 
 
-def cpu_baseline(wl: Workload, budget_heads: int):
-    """The oracle, as it stands, on the first heads of the same workload (bounded CPU sample)."""
+def cpu_baseline(wl: Workload, budget_heads: int, max_tokens: int):
+    """The oracle, as it stands, timed on a bounded sample of the same workload: the first heads and
+    the first `max_tokens` tokens (for a causal mask the leading tokens form a closed sub-problem)."""
     import torch
     from oracle import attention as OA
     q, k, v, do = wl.host
-    heads = [(0, h) for h in range(min(wl.H, budget_heads))]
-    r = lambda x: torch.from_numpy(x[:, : len(heads)]).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
+    nh = min(wl.H, budget_heads)
+    n = min(wl.N, max_tokens)
+    r = lambda x: torch.from_numpy(np.ascontiguousarray(x[:1, :nh, :n])).to(torch.bfloat16).to(  # noqa: E731
+        torch.float64).numpy()
     qs, ks, vs, dos = (r(x) for x in (q, k, v, do))
-    sub = W.MaskSpec(wl.N, 1, wl.spec.Hm if wl.spec.Hm == 1 else len(heads), wl.spec.causal,
-                     *[None if x is None else x[:1, : (1 if wl.spec.Hm == 1 else len(heads))]
-                       for x in wl.spec.vectors()])
-    workers = min(len(heads), 16, os.cpu_count() or 1)
+    hm = 1 if wl.spec.Hm == 1 else nh
+    sub = W.MaskSpec(n, 1, hm, wl.spec.causal,
+                     *[None if x is None else np.ascontiguousarray(x[:1, :hm, :n]) for x in wl.spec.vectors()])
+    workers = min(nh, 16, os.cpu_count() or 1)
     t0 = time.perf_counter()
     _, _, _, _, _, used = OA.fwd_bwd(qs, ks, vs, dos, sub.vectors(), sub.causal, wl.scale, sub.Hm, workers=workers)
     dt = time.perf_counter() - t0
-    U = unmasked_pairs(sub, len(heads))
+    U = unmasked_pairs(sub, nh)
     flop = 14.0 * wl.d * U
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
-            "sample": f"{len(heads)} of {wl.H} heads of {wl.name} (fp64 NumPy fwd+bwd), {dt:.1f} s",
-            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+            "sample": f"heads 0..{nh - 1} of {wl.H}, tokens 0..{n - 1} of {wl.N} of {wl.name} "
+                      f"(fp64 NumPy fwd+bwd, U={U}), {dt:.1f} s",
+            "seconds": round(dt, 2), "cpu": platform.processor() or platform.machine()}
 
 
 def main():
@@ -173,7 +210,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -218,12 +257,21 @@ def main():
         "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[1] * 1e-3) / 1e12, 2),
                          "fm_bwd": round(bwd_tflops, 2)},
         "finite_outputs": ok,
-        "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_pre + bwd_main + bwd_dq launches)",
+        "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_pre, bwd_pair, bwd_dq launches)",
                      "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(wl.name),
+                     "flop_per_call": wl.flop_bwd, "flop_formula": "10*d*U"},
     }
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of float32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads, args.cpu_tokens)
     if args.sweep:
         sweep = {}
         for name in WORKLOADS:
