@@ -88,16 +88,17 @@ fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, in
                  const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
                  const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream);
 
-/* Device workspace fm_bwd needs: a float32 [B, H, N, d] dq accumulator plus a float32 [B, H, N] row
- * term D_i = sum_k dout_ik out_ik, each 256-byte aligned. 0 on bad sizes. */
+/* Device workspace fm_bwd needs: the float32 [B, H, N] row term D_i = sum_k dout_ik out_ik, rounded up
+ * to 256 bytes. 0 on bad sizes. */
 size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d);
 
 /* Backward pass: gradients of sum(out * dout) with out from fm_fwd on the same inputs and mask.
  *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
- * with P recomputed from q, k and the forward's lse. Key tiles run in parallel; each accumulates its
- * dk/dv tile on chip and adds its dq contribution into the float32 workspace accumulator, which a
- * final pass rounds into dq. dq, dk, dv have `dtype`. The workspace is overwritten (its previous
- * content does not matter) and must not be shared by concurrent calls.
+ * with P recomputed from q, k and the forward's lse. A query-tile-parallel pass forms D and dq (each
+ * query tile accumulates its dq rows on chip over the live key tiles); a key-tile-parallel pass then
+ * forms dk and dv (each key tile accumulates on chip over the live query tiles). No atomics: the result
+ * is bitwise reproducible. dq, dk, dv have `dtype`. The workspace receives D (its previous content does
+ * not matter) and must not be shared by concurrent calls.
  * Errors: FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_LAUNCH. */
 fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, fm_dtype dtype, int B, int H, int N, int d,

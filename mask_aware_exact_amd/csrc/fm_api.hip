@@ -16,9 +16,9 @@ hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const v
                       const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
                       int N, int Hm, int causal, float scale, hipStream_t stream);
 hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
-                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* dd,
-                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B,
-                      int H, int N, int Hm, int causal, float scale, hipStream_t stream);
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
+                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int N, int Hm,
+                      int causal, float scale, hipStream_t stream);
 int fwd_qblock();
 }  // namespace fm
 
@@ -91,7 +91,7 @@ fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, in
 size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d) {
   if (dtype_d_ok(dtype, d) != FM_OK || !sizes_ok(B, H, N)) return 0;
   const size_t rows = (size_t)B * H * N;
-  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+  return round_up(rows * sizeof(float));
 }
 
 fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
@@ -111,11 +111,9 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
     if (!aligned16(p)) return FM_ERR_INVALID;
   const size_t need = fm_bwd_workspace_bytes(dtype, B, H, N, d);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FM_ERR_WORKSPACE;
-  const size_t rows = (size_t)B * H * N;
-  float* dq_acc = static_cast<float*>(workspace);
-  float* dd = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * sizeof(float)));
-  return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts,
-                                 ute, bounds, B, H, N, Hm, causal != 0, scale, stream));
+  float* dd = static_cast<float*>(workspace);
+  return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dd, lts, lte, uts, ute,
+                                 bounds, B, H, N, Hm, causal != 0, scale, stream));
 }
 
 fm_status fm_tile_classes(const int32_t* bounds, int B, int Hm, int N, int causal, int qblock, uint8_t* classes,

@@ -2,64 +2,29 @@
 //
 // The gradient of sum(out * dO) through softmax attention, recomputing P from q, k and the forward's
 // lse, with tiles the mask covers completely skipped (FlashMask abstract, papers.pytorch.kr
-// 2410.01359). Three kernels run in order on the caller's stream:
-//  1. bwd_pre:  D_i = sum_d dO_id out_id (float32) per row, and the float32 dq accumulator cleared.
-//  2. bwd_main: one workgroup per (b, h, key tile of BC = 128 columns); wave w owns keys 32 w .. 32 w+31
-//     (one key column per lane). The live query tiles (not fully masked for this key tile) are found
-//     64 at a time with a wave ballot; the next one is loaded into registers while the current one is
-//     computed, and Q / dO are double-buffered row-major in LDS. Per live query tile of BR rows:
-//       S = Q K^T and dP = dO V^T with K, V held in registers (keys as the N axis, so every lane keeps
-//       one key column and its four mask values in registers);
-//       P = exp(S - lse) (0 where masked), dS = P o (dP - D);
-//       dV^T += dO^T P and dK^T += Q^T dS, the k axis (query rows) read from the row-major Q / dO
-//       tiles through transposing LDS reads, accumulated on chip for the whole query loop;
-//       dS goes to LDS, and each wave forms dQ = dS K for one 32-wide d block over the workgroup's
-//       128 keys, with that block of K held in registers (loaded once), and adds it into the float32
-//       accumulator with hardware float atomics (one 128-byte row segment per instruction).
-//  3. bwd_dq:   dq = accumulator rounded to the input type.
+// 2410.01359). Two kernels run in order on the caller's stream, and neither uses atomics:
+//  1. bwd_dq: query-tile parallel, laid out like the forward (one query row per lane). Per live key
+//     tile it forms S^T = K Q^T and dP^T = V dO^T, then P = exp(S - lse) (0 where masked) and
+//     dS = P o (dP - D), and accumulates dQ^T += K^T dS^T with dS^T straight from registers. It also
+//     forms D_i = sum_d dO_id out_id for its rows and stores it for kernel 2.
+//  2. bwd_dkdv: key-tile parallel. Per live query tile it forms S, dP, P and dS with one key column
+//     per lane and accumulates dV^T += dO^T P and dK^T += Q^T dS on chip for the whole query loop.
+// Recomputing S and dP in kernel 1 costs 4 d FLOP per unmasked pair more than adding partial dQ tiles
+// from kernel 2 with float atomics, whose traffic (one float32 dQ tile per live tile pair) was
+// measured to cost more than that on MI355X.
 #include "fm_common.h"
 
 namespace fm {
-
-// ------------------------------------------------------------------ 1. D and accumulator clear
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ dout,
-                                                      float* __restrict__ dd, float* __restrict__ dq_acc,
-                                                      long rows) {
-  constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
-  constexpr int EPC = 16 / (int)sizeof(T);      // elements per chunk
-  constexpr int RPB = 256 / CPR;                // rows per block
-  constexpr int ACC_CHUNKS = D * 4 / 16 / CPR;  // 16-byte accumulator chunks per lane
-  const int tid = threadIdx.x;
-  const long row = (long)blockIdx.x * RPB + tid / CPR;
-  const int c = tid % CPR;
-  float part = 0.f;
-  if (row < rows) {
-    const T* po = out + row * D + c * EPC;
-    const T* pd = dout + row * D + c * EPC;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) part += (float)po[e] * (float)pd[e];
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < ACC_CHUNKS; ++k)
-      *reinterpret_cast<f32x4*>(dq_acc + row * D + (c * ACC_CHUNKS + k) * 4) = z;
-  }
-#pragma unroll
-  for (int m = CPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-  if (row < rows && c == 0) dd[row] = part;
-}
-
-// ------------------------------------------------------------------ 2. main key-tile-parallel kernel
 
 struct BwdArgs {
   const void* q;
   const void* k;
   const void* v;
+  const void* out;
   const void* dout;
   const float* lse;
-  const float* dd;
-  float* dq_acc;
+  float* dd;  // D_i, written by bwd_dq, read by bwd_dkdv
+  void* dq;
   void* dk;
   void* dv;
   const int* lts;
@@ -68,44 +33,38 @@ struct BwdArgs {
   const int* ute;
   const int* bounds;
   int B, H, N, Hm;
-  int nkt;  // key tiles of BC per head
   int nkb;  // bounds entries per (b, hm) row
   int causal;
   float scale;
   float scale_log2;
 };
 
+// ------------------------------------------------------------------ 1. dQ (and D), query-tile parallel
+
 template <typename T, int D>
-struct BwdTraits {
-  static constexpr int BC = 128;                         // keys per workgroup
-  static constexpr int BR = sizeof(T) == 2 ? 64 : 32;    // query rows per iteration
+struct DqTraits {
+  static constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
+  static constexpr int BC = 64;   // keys per tile (one bounds entry)
   static constexpr int NT = 256;
-  static constexpr int PITCH = D + 16 / (int)sizeof(T);  // row-major Q / dO / K tiles
-  static constexpr int PS = BR + 16 / (int)sizeof(T);    // dS tile [key][row]
-  static constexpr int NKF = D / MM<T>::KW;              // K / V fragments per lane (k = d)
-  static constexpr int NIB = BR / 32;                    // 32-row blocks per query tile
-  static constexpr int NDB = D / 32;                     // 32-wide d blocks
-  static constexpr int TPB = 16 / MM<T>::E;              // products per 32 k values
-  static constexpr int NKQ = BC / 32 * TPB;              // products over the workgroup's keys (dQ)
-  static constexpr int WPD = 4 / NDB;                    // waves sharing one d block in dQ
-  static constexpr int CPR = D * (int)sizeof(T) / 16;    // 16-byte chunks per row
-  static constexpr int CH = BR * CPR / NT;               // chunks per thread per Q / dO tile
-  static_assert(BC * CPR % NT == 0 && CH >= 1, "tile copies must divide evenly");
+  static constexpr bool SWZ = sizeof(T) == 2;            // bf16 K tile: swizzled, unpadded
+  static constexpr int KP = SWZ ? D : D + 4;             // K row pitch (elements)
+  static constexpr int VP = D + 16 / (int)sizeof(T);     // V row pitch: 16-byte padding (row reads only)
+  static constexpr int NQF = D / MM<T>::KW;
+  static constexpr int NDB = D / 32;
+  static constexpr int TPB = 16 / MM<T>::E;
+  static constexpr int CPR = D * (int)sizeof(T) / 16;
+  static constexpr int CH = BC * CPR / NT;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
-  using Tr = BwdTraits<T, D>;
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using Tr = DqTraits<T, D>;
   using M = MM<T>;
-  constexpr int BC = Tr::BC, BR = Tr::BR, PITCH = Tr::PITCH, PS = Tr::PS, CPR = Tr::CPR, CH = Tr::CH;
-  // q_lds / do_lds hold two query tiles each (double buffer); at start-up the same memory holds the K tile.
-  static_assert(4 * BR >= BC, "the K tile is staged through the query-tile buffers");
-  __shared__ __attribute__((aligned(16))) T qdo_lds[4 * BR * PITCH];
-  T* const q_lds = qdo_lds;
-  T* const do_lds = qdo_lds + 2 * BR * PITCH;
-  __shared__ __attribute__((aligned(16))) T ds_lds[BC * PS];
-  __shared__ __attribute__((aligned(16))) float lse_lds[2][BR];
-  __shared__ __attribute__((aligned(16))) float dd_lds[2][BR];
+  constexpr int BR = Tr::BR, BC = Tr::BC, KP = Tr::KP, VP = Tr::VP, CPR = Tr::CPR, CH = Tr::CH;
+  constexpr bool SWZ = Tr::SWZ;
+  __shared__ __attribute__((aligned(16))) T k_lds[2][BC * KP];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VP];
+  __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -114,25 +73,23 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
   const int l32 = lane & 31;
 
   const int BH = a.B * a.H;
+  const int nq = (a.N + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
-  const int kt = (int)(blockIdx.x / BH);  // early key tiles carry the most causal work: dispatch them first
+  const int qt = nq - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) query tiles first
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
   const int N = a.N;
-  const int c0 = kt * BC;
-  const int c1 = min(N, c0 + BC);
-  const int jl = wave * 32 + l32;  // this lane's key column inside the tile
-  const int j = c0 + jl;
+  const int r0 = qt * BR;
+  const int r1 = min(N, r0 + BR);
+  const int row = r0 + wave * 32 + l32;  // this lane's query row
 
   const size_t head = (size_t)bh * N * D;
   const T* __restrict__ qg = static_cast<const T*>(a.q) + head;
   const T* __restrict__ kg = static_cast<const T*>(a.k) + head;
   const T* __restrict__ vg = static_cast<const T*>(a.v) + head;
+  const T* __restrict__ og = static_cast<const T*>(a.out) + head;
   const T* __restrict__ dog = static_cast<const T*>(a.dout) + head;
-  const float* __restrict__ lseg = a.lse + (size_t)bh * N;
-  const float* __restrict__ ddg = a.dd + (size_t)bh * N;
-  float* __restrict__ dqg = a.dq_acc + head;
   const size_t vrow = ((size_t)b * a.Hm + hm) * N;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
   const bool has_lt = a.lts != nullptr;
@@ -140,268 +97,218 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
   const bool causal = a.causal != 0;
   const float sl2 = a.scale_log2;
 
-  // This lane's key column: mask values and K / V fragments with k = d (operand B of S and dP).
-  int m_lts = 0, m_lte = 0, m_uts = 0, m_ute = 0;
-  typename M::frag kf[Tr::NKF], vf[Tr::NKF];
-  if (j < N) {
-    if (has_lt) { m_lts = a.lts[vrow + j]; m_lte = a.lte[vrow + j]; }
-    if (has_ut) { m_uts = a.uts[vrow + j]; m_ute = a.ute[vrow + j]; }
+  // Q^T and dO^T operands (k = d) for this lane's row, D_i and lse_i.
+  typename M::frag qf[Tr::NQF], df[Tr::NQF];
+  float part = 0.f;
 #pragma unroll
-    for (int c = 0; c < Tr::NKF; ++c) {
-      kf[c] = load_kcontig_frag<T>(kg + (size_t)j * D + c * M::KW + g * M::E);
-      vf[c] = load_kcontig_frag<T>(vg + (size_t)j * D + c * M::KW + g * M::E);
-    }
-  } else {
+  for (int c = 0; c < Tr::NQF; ++c) {
+    if (row < N) {
+      const size_t e = (size_t)row * D + c * M::KW + g * M::E;
+      qf[c] = load_kcontig_frag<T>(qg + e);
+      df[c] = load_kcontig_frag<T>(dog + e);
+      const typename M::frag of = load_kcontig_frag<T>(og + e);
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int c = 0; c < Tr::NKF; ++c) {
-      kf[c] = typename M::frag{};
-      vf[c] = typename M::frag{};
+        for (int s = 0; s < 8; ++s) part += (float)df[c][s] * (float)of[s];
+      } else {
+        part += df[c] * of;
+      }
+    } else {
+      qf[c] = typename M::frag{};
+      df[c] = typename M::frag{};
     }
   }
-
-  // K fragments with k = key (operand B of dQ = dS K) for this wave's 32-wide d block, read once
-  // through the LDS from the row-major K tile.
-  const int wd = wave % Tr::NDB;
-  load_tile<T, BC, D, PITCH, Tr::NT>(q_lds, kg, c0, N, tid);
-  __syncthreads();
-  typename M::frag kq[Tr::NKQ];
-#pragma unroll
-  for (int t = 0; t < Tr::NKQ; ++t) kq[t] = load_kmajor_frag<T>(q_lds, PITCH, 0, wd * 32, t, lane);
-  __syncthreads();
-
-  f32x16 dk[Tr::NDB], dv[Tr::NDB];
-#pragma unroll
-  for (int db = 0; db < Tr::NDB; ++db) {
-    dk[db] = zero16();
-    dv[db] = zero16();
+  const float Di = part + __shfl_xor(part, 32, 64);
+  float lse2 = INFINITY;  // rows past N or without any unmasked key: exp(S - lse) = 0
+  if (row < N) {
+    const float l = a.lse[(size_t)bh * N + row];
+    lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
+    if (g == 0) a.dd[(size_t)bh * N + row] = Di;
   }
 
-  int bnd[8];
-  merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N, bnd);
-  const int nq = (N + BR - 1) / BR;
-  const int qt_begin = causal ? c0 / BR : 0;
-  auto class_of = [&](int qt) { return classify_tile(qt * BR, min(N, qt * BR + BR), c0, c1, bnd, causal); };
+  f32x16 acc[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) acc[db] = zero16();
 
-  // Prefetch registers for one query tile.
-  i32x4 qr[CH], dr[CH];
-  float lr = 0.f, ddr = 0.f;
-  auto fetch = [&](int qt) {
-    const int q0 = qt * BR;
+  SwzRowReads<D> krd;
+  SwzColReads<D> kcd;
+  if constexpr (SWZ) {
+    krd.init(lane);
+    kcd.init(lane);
+  }
+
+  const int nkt = (N + BC - 1) / BC;
+  const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
+
+  i32x4 kr[CH], vr[CH];
+  i32x4 mr = {0, 0, 0, 0};
+  auto fetch = [&](int kt) {
+    const int c0 = kt * BC;
 #pragma unroll
     for (int it = 0; it < CH; ++it) {
       const int c = it * Tr::NT + tid;
       const int r = c / CPR, cc = c % CPR;
-      qr[it] = i32x4{0, 0, 0, 0};
-      dr[it] = i32x4{0, 0, 0, 0};
-      if (q0 + r < N) {
-        qr[it] = ld16(reinterpret_cast<const char*>(qg + (size_t)(q0 + r) * D) + cc * 16);
-        dr[it] = ld16(reinterpret_cast<const char*>(dog + (size_t)(q0 + r) * D) + cc * 16);
-      }
+      const bool ok = c0 + r < N;
+      const size_t rr = ok ? (size_t)(c0 + r) : 0;
+      kr[it] = ld16(reinterpret_cast<const char*>(kg + rr * D) + cc * 16);
+      vr[it] = ld16(reinterpret_cast<const char*>(vg + rr * D) + cc * 16);
     }
-    if (tid < BR) {
-      const int i = q0 + tid;
-      lr = i < N ? lseg[i] : INFINITY;
-      ddr = i < N ? ddg[i] : 0.f;
+    if (tid < BC) {
+      const int j = c0 + tid;
+      mr = i32x4{0, 0, 0, 0};
+      if (j < N) {
+        if (has_lt) { mr[0] = a.lts[vrow + j]; mr[1] = a.lte[vrow + j]; }
+        if (has_ut) { mr[2] = a.uts[vrow + j]; mr[3] = a.ute[vrow + j]; }
+      }
     }
   };
   auto stash = [&](int buf) {
-    T* qb = q_lds + buf * BR * PITCH;
-    T* db_ = do_lds + buf * BR * PITCH;
 #pragma unroll
     for (int it = 0; it < CH; ++it) {
       const int c = it * Tr::NT + tid;
       const int r = c / CPR, cc = c % CPR;
-      st16(reinterpret_cast<char*>(qb + r * PITCH) + cc * 16, qr[it]);
-      st16(reinterpret_cast<char*>(db_ + r * PITCH) + cc * 16, dr[it]);
+      if constexpr (SWZ) {
+        st16(reinterpret_cast<char*>(k_lds[buf]) + swz_off<D>(r, cc * 8), kr[it]);
+      } else {
+        st16(reinterpret_cast<char*>(&k_lds[buf][r * KP]) + cc * 16, kr[it]);
+      }
+      st16(reinterpret_cast<char*>(&v_lds[buf][r * VP]) + cc * 16, vr[it]);
     }
-    if (tid < BR) {
-      // a row without any unmasked key has lse = -inf; +inf makes exp(S - lse) = 0 for it
-      const float l = (lr == -INFINITY) ? INFINITY : lr;
-      lse_lds[buf][tid] = l * LOG2E;
-      dd_lds[buf][tid] = ddr;
-    }
+    if (tid < BC) vec_lds[buf][tid] = mr;
   };
 
+  auto class_of = [&](int t) {
+    int bt[8];
+    merged_bounds(brow, t, t + 1, N, bt);
+    return classify_tile(r0, r1, t * BC, min(N, t * BC + BC), bt, causal);
+  };
   TileWindow win = empty_window();
-  int qt = next_live_tile(win, qt_begin, nq, class_of, lane);
-  if (qt < nq) fetch(qt);
+  int kt = next_live_tile(win, 0, kt_end, class_of, lane);
+  if (kt < kt_end) fetch(kt);
   int buf = 0;
 
-  while (qt < nq) {
-    const int q0 = qt * BR;
-    const bool need_mask = window_partial(win, qt) || (q0 + BR > N) || (c0 + BC > N);
+  while (kt < kt_end) {
+    const int c0 = kt * BC;
+    const bool need_mask = window_partial(win, kt) || (c0 + BC > N);
     stash(buf);
-    __syncthreads();  // (A) this tile is in LDS; every wave is past the previous tile's dQ phase
-    const int qt_next = next_live_tile(win, qt + 1, nq, class_of, lane);
-    if (qt_next < nq) fetch(qt_next);
+    __syncthreads();
+    const int kt_next = next_live_tile(win, kt + 1, kt_end, class_of, lane);
+    if (kt_next < kt_end) fetch(kt_next);
 
-    const T* qb = q_lds + buf * BR * PITCH;
-    const T* dob = do_lds + buf * BR * PITCH;
-    // S = Q K^T and dP = dO V^T: rows = this tile's queries, columns = this wave's keys.
-    f32x16 s[Tr::NIB], dp[Tr::NIB];
+    const T* kt_lds = k_lds[buf];
+    const T* vt_lds = v_lds[buf];
+    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks (rows = keys, columns = queries).
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int ib = 0; ib < Tr::NIB; ++ib) {
-      s[ib] = zero16();
-      dp[ib] = zero16();
-      const T* qrow = qb + (ib * 32 + l32) * PITCH + g * M::E;
-      const T* dorow = dob + (ib * 32 + l32) * PITCH + g * M::E;
+    for (int jb = 0; jb < 2; ++jb) {
+      s[jb] = zero16();
+      dp[jb] = zero16();
+      const T* vrow_l = vt_lds + (jb * 32 + l32) * VP + g * M::E;
 #pragma unroll
-      for (int c = 0; c < Tr::NKF; ++c) {
-        s[ib] = M::mma(load_kcontig_frag<T>(qrow + c * M::KW), kf[c], s[ib]);
-        dp[ib] = M::mma(load_kcontig_frag<T>(dorow + c * M::KW), vf[c], dp[ib]);
+      for (int c = 0; c < Tr::NQF; ++c) {
+        if constexpr (SWZ) {
+          s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
+        } else {
+          s[jb] = M::mma(load_kcontig_frag<T>(kt_lds + (jb * 32 + l32) * KP + g * M::E + c * M::KW), qf[c], s[jb]);
+        }
+        dp[jb] = M::mma(load_kcontig_frag<T>(vrow_l + c * M::KW), df[c], dp[jb]);
       }
     }
-
-    // P and dS in place (s <- P, dp <- dS). Masked rows of this lane's key column come from a bitmap.
-    const uint64_t mbits = need_mask ? masked_row_bits(q0, j, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute)
-                                     : 0ull;
-    const uint64_t mg = mbits >> (4 * g);
+    // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0.
 #pragma unroll
-    for (int ib = 0; ib < Tr::NIB; ++ib) {
+    for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int il0 = ib * 32 + 8 * q4 + 4 * g;
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
-        const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[buf][il0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q4 + e;
-          float p = __builtin_amdgcn_exp2f(s[ib][r] * sl2 - lse4[e]);
-          p = ((mg >> (ib * 32 + 8 * q4 + e)) & 1) ? 0.f : p;
-          s[ib][r] = p;
-          dp[ib][r] = p * (dp[ib][r] - dd4[e]);
+          float p = __builtin_amdgcn_exp2f(s[jb][r] * sl2 - lse2);
+          if (need_mask) {
+            const int jl = jb * 32 + 8 * q4 + 4 * g + e;
+            const i32x4 mv = vec_lds[buf][jl];
+            const bool msk =
+                (c0 + jl >= N) | masked_elem(row, c0 + jl, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
+            p = msk ? 0.f : p;
+          }
+          dp[jb][r] = p * (dp[jb][r] - Di);
         }
       }
     }
-
-    // dV^T += dO^T P and dK^T += Q^T dS (k = query rows of the tile).
+    // dQ^T += K^T dS^T over the 64 keys of the tile.
 #pragma unroll
-    for (int t = 0; t < Tr::NIB * Tr::TPB; ++t) {
-      const typename M::frag pf = acc_frag<T>(s[t / Tr::TPB], t % Tr::TPB);
+    for (int t = 0; t < 2 * Tr::TPB; ++t) {
       const typename M::frag sf = acc_frag<T>(dp[t / Tr::TPB], t % Tr::TPB);
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
-        dv[db] = M::mma(load_kmajor_frag<T>(dob, PITCH, 0, db * 32, t, lane), pf, dv[db]);
-        dk[db] = M::mma(load_kmajor_frag<T>(qb, PITCH, 0, db * 32, t, lane), sf, dk[db]);
-      }
-    }
-
-    // dS to LDS as [key][row], rounded to T.
-#pragma unroll
-    for (int ib = 0; ib < Tr::NIB; ++ib) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int il0 = ib * 32 + 8 * q4 + 4 * g;
-        T* dst = ds_lds + jl * PS + il0;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)dp[ib][4 * q4 + e];
-          *reinterpret_cast<bf16x4*>(dst) = w;
+        if constexpr (SWZ) {
+          acc[db] = M::mma(kcd.read(kt_lds, t, db), sf, acc[db]);
         } else {
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = dp[ib][4 * q4 + e];
-          *reinterpret_cast<f32x4*>(dst) = w;
+          acc[db] = M::mma(load_kmajor_frag<T>(kt_lds, KP, 0, db * 32, t, lane), sf, acc[db]);
         }
       }
     }
-    __syncthreads();  // (B) dS of all four waves is in LDS
-
-    // dQ rows += scale * dS K over the workgroup's keys, for this wave's d block.
-#pragma unroll
-    for (int ib = wave / Tr::NDB; ib < Tr::NIB; ib += Tr::WPD) {
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int t = 0; t < Tr::NKQ; ++t) acc = M::mma(load_kmajor_frag<T>(ds_lds, PS, 0, ib * 32, t, lane), kq[t], acc);
-      float* dst = dqg + (size_t)(q0 + ib * 32 + 4 * g) * D + wd * 32 + l32;
-      if (q0 + BR <= N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r] * a.scale);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = q0 + ib * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (i < N) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r] * a.scale);
-        }
-      }
-    }
-    qt = qt_next;
+    kt = kt_next;
     buf ^= 1;
   }
 
-  // dK = scale * dK^T, dV = dV^T for this lane's key column.
-  if (j < N) {
-    T* dkg = static_cast<T*>(a.dk) + head + (size_t)j * D;
-    T* dvg = static_cast<T*>(a.dv) + head + (size_t)j * D;
+  // dq = scale * dQ^T for this lane's row.
+  if (row < N) {
+    T* dqg = static_cast<T*>(a.dq) + head + (size_t)row * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = db * 32 + 8 * q4 + 4 * g;
         if constexpr (sizeof(T) == 2) {
-          bf16x4 wk, wv;
+          bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            wk[e] = (bf16)(dk[db][4 * q4 + e] * a.scale);
-            wv[e] = (bf16)dv[db][4 * q4 + e];
-          }
-          *reinterpret_cast<bf16x4*>(dkg + d0) = wk;
-          *reinterpret_cast<bf16x4*>(dvg + d0) = wv;
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * q4 + e] * a.scale);
+          *reinterpret_cast<bf16x4*>(dqg + d0) = w;
         } else {
-          f32x4 wk, wv;
+          f32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            wk[e] = dk[db][4 * q4 + e] * a.scale;
-            wv[e] = dv[db][4 * q4 + e];
-          }
-          *reinterpret_cast<f32x4*>(dkg + d0) = wk;
-          *reinterpret_cast<f32x4*>(dvg + d0) = wv;
+          for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * q4 + e] * a.scale;
+          *reinterpret_cast<f32x4*>(dqg + d0) = w;
         }
       }
     }
   }
 }
 
-// ------------------------------------------------------------------ 2b. bf16 main kernel, wave pairs
+// ------------------------------------------------------------------ 2a. dK / dV, bf16, wave pairs
 
-// bf16 variant of the key-tile-parallel kernel with eight waves: waves w and w + 4 share the 32 keys of
-// group w % 4 and split the work so that each keeps fewer than 256 registers (two waves per SIMD):
+// Eight waves per 128-key tile: waves w and w + 4 share the 32 keys of group w % 4 and split the work so
+// that each stays under 256 registers (two waves per SIMD):
 //   role 0 (w < 4) holds K, forms S = Q K^T and P, and writes P to LDS;
 //   role 1 (w >= 4) holds V, forms dP = dO V^T, reads P back, forms dS and writes it to LDS;
-//   each role accumulates dV and dK for one half of the d columns, and every wave then forms one
-//   32 x 32 block of dQ = dS K over the workgroup's 128 keys.
+//   each role accumulates dV and dK for one half of the d columns.
 // While one wave of a SIMD runs its exponentials or dS arithmetic the other issues matrix products.
 template <int D>
 struct PairTraits {
   static constexpr int BC = 128;          // keys per workgroup
   static constexpr int BR = 64;           // query rows per iteration
   static constexpr int NT = 512;
-  static constexpr int PITCH = D + 8;     // row-major Q / dO / K tiles (16-byte row padding)
   static constexpr int PS = BR + 8;       // P and dS tiles [key][row]
   static constexpr int NKF = D / 16;      // K or V fragments per lane (k = d)
   static constexpr int NDB = D / 32;      // 32-wide d blocks
   static constexpr int HDB = NDB / 2;     // d blocks per role
-  static constexpr int NQB = 2 * NDB;     // dQ blocks per query tile
   static constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
   static constexpr int CH = BR * CPR / NT;
-  static_assert(BR * CPR % NT == 0 && BC * CPR % NT == 0, "tile copies must divide evenly");
+  static_assert(BR * CPR % NT == 0, "tile copies must divide evenly");
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Tr = PairTraits<D>;
   using M = MM<bf16>;
-  constexpr int BC = Tr::BC, BR = Tr::BR, PITCH = Tr::PITCH, PS = Tr::PS, CPR = Tr::CPR, CH = Tr::CH;
-  static_assert(4 * BR * D >= BC * PITCH, "the K tile is staged through the query-tile buffers");
+  constexpr int BC = Tr::BC, BR = Tr::BR, PS = Tr::PS, CPR = Tr::CPR, CH = Tr::CH;
   // Q and dO tiles are swizzled and unpadded (rows of D elements), two of each (double buffer).
-  __shared__ __attribute__((aligned(16))) bf16 qdo_lds[4 * BR * D];
+  __shared__ __attribute__((aligned(16))) bf16 q_lds[2 * BR * D];
+  __shared__ __attribute__((aligned(16))) bf16 do_lds[2 * BR * D];
   __shared__ __attribute__((aligned(16))) bf16 p_lds[BC * PS];
   __shared__ __attribute__((aligned(16))) bf16 ds_lds[BC * PS];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BR];
   __shared__ __attribute__((aligned(16))) float dd_lds[2][BR];
-  bf16* const q_lds = qdo_lds;
-  bf16* const do_lds = qdo_lds + 2 * BR * D;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -430,7 +337,6 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
   const bf16* __restrict__ dog = static_cast<const bf16*>(a.dout) + head;
   const float* __restrict__ lseg = a.lse + (size_t)bh * N;
   const float* __restrict__ ddg = a.dd + (size_t)bh * N;
-  float* __restrict__ dqg = a.dq_acc + head;
   const size_t vrow = ((size_t)b * a.Hm + hm) * N;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
   const bool has_lt = a.lts != nullptr;
@@ -453,18 +359,10 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
       for (int c = 0; c < Tr::NKF; ++c) xf[c] = bf16x8{};
     }
   }
-
-  // dQ block of this wave (if any) and its K fragments with k = key, read once through the LDS.
-  const int ob = wave;
-  const bool has_dq = ob < Tr::NQB;
-  const int dq_ib = ob / Tr::NDB;
-  const int dq_db = ob % Tr::NDB;
-  load_tile<bf16, BC, D, PITCH, Tr::NT>(qdo_lds, kg, c0, N, tid);
-  __syncthreads();
-  bf16x8 kq[BC / 16];
-#pragma unroll
-  for (int t = 0; t < BC / 16; ++t) kq[t] = load_kmajor_frag<bf16>(qdo_lds, PITCH, 0, dq_db * 32, t, lane);
-  __syncthreads();
+  SwzRowReads<D> rrd;
+  SwzColReads<D> crd;
+  rrd.init(lane);
+  crd.init(lane);
 
   f32x16 dk[Tr::HDB], dv[Tr::HDB];
 #pragma unroll
@@ -480,27 +378,27 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
   const int qt_begin = causal ? c0 / BR : 0;
   auto class_of = [&](int qt) { return classify_tile(qt * BR, min(N, qt * BR + BR), c0, c1, bnd, causal); };
 
+  // Prefetch registers for one query tile. Loads are unconditional (rows past N read row N - 1, whose
+  // values are finite; those rows get lse = +inf and are masked, so they contribute nothing) so that
+  // nothing waits on them before the next iteration stores them.
   i32x4 qr[CH], dr[CH];
   float lr = 0.f, ddr = 0.f;
+  int l_row = 0;
   auto fetch = [&](int qt) {
     const int q0 = qt * BR;
 #pragma unroll
     for (int it = 0; it < CH; ++it) {
       const int c = it * Tr::NT + tid;
       const int r = c / CPR, cc = c % CPR;
-      const bool ok = q0 + r < N;
-      const int rr = ok ? q0 + r : 0;
-      qr[it] = ld16(reinterpret_cast<const char*>(qg + (size_t)rr * D) + cc * 16);
-      dr[it] = ld16(reinterpret_cast<const char*>(dog + (size_t)rr * D) + cc * 16);
-      if (!ok) {
-        qr[it] = i32x4{0, 0, 0, 0};
-        dr[it] = i32x4{0, 0, 0, 0};
-      }
+      const size_t rr = (size_t)min(q0 + r, N - 1);
+      qr[it] = ld16(reinterpret_cast<const char*>(qg + rr * D) + cc * 16);
+      dr[it] = ld16(reinterpret_cast<const char*>(dog + rr * D) + cc * 16);
     }
     if (tid < BR) {
-      const int i = q0 + tid;
-      lr = i < N ? lseg[i] : INFINITY;
-      ddr = i < N ? ddg[i] : 0.f;
+      l_row = q0 + tid;
+      const int i = min(l_row, N - 1);
+      lr = lseg[i];
+      ddr = ddg[i];
     }
   };
   auto stash = [&](int buf) {
@@ -514,8 +412,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
       st16(db_ + swz_off<D>(r, cc * 8), dr[it]);
     }
     if (tid < BR) {
-      // a row without any unmasked key has lse = -inf; +inf makes exp(S - lse) = 0 for it
-      const float l = (lr == -INFINITY) ? INFINITY : lr;
+      // rows past N and rows without any unmasked key (lse = -inf) get +inf: exp(S - lse) = 0 for them
+      const float l = (l_row >= N || lr == -INFINITY) ? INFINITY : lr;
       lse_lds[buf][tid] = l * LOG2E;
       dd_lds[buf][tid] = ddr;
     }
@@ -544,27 +442,39 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
     for (int ib = 0; ib < 2; ++ib) {
       x[ib] = zero16();
 #pragma unroll
-      for (int c = 0; c < Tr::NKF; ++c)
-        x[ib] = M::mma(swz_kcontig<D>(xb, ib * 32 + l32, c * 16 + g * 8), xf[c], x[ib]);
+      for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(xb, ib, c), xf[c], x[ib]);
     }
     bf16x4 pv[2][4];  // P (role 0: computed, role 1: read back), register order
     if (role == 0) {
-      const uint64_t mbits =
-          need_mask ? masked_row_bits(q0, j, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute) : 0ull;
-      const uint64_t mg = mbits >> (4 * g);
+      if (need_mask) {
+        const uint64_t mbits = masked_row_bits(q0, j, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
+        const uint32_t mlo = (uint32_t)(mbits >> (4 * g)), mhi = (uint32_t)(mbits >> (32 + 4 * g));
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+        for (int ib = 0; ib < 2; ++ib) {
+          const uint32_t mw = ib == 0 ? mlo : mhi;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int il0 = ib * 32 + 8 * q4 + 4 * g;
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int il0 = ib * 32 + 8 * q4 + 4 * g;
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float p = __builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
-            p = ((mg >> (ib * 32 + 8 * q4 + e)) & 1) ? 0.f : p;
-            pv[ib][q4][e] = (bf16)p;
+            for (int e = 0; e < 4; ++e) {
+              const float p = __builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
+              pv[ib][q4][e] = (bf16)(((mw >> (8 * q4 + e)) & 1u) ? 0.f : p);
+            }
+            *reinterpret_cast<bf16x4*>(p_lds + jl * PS + il0) = pv[ib][q4];
           }
-          *reinterpret_cast<bf16x4*>(p_lds + jl * PS + il0) = pv[ib][q4];
+        }
+      } else {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int il0 = ib * 32 + 8 * q4 + 4 * g;
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[ib][q4][e] = (bf16)__builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
+            *reinterpret_cast<bf16x4*>(p_lds + jl * PS + il0) = pv[ib][q4];
+          }
         }
       }
     }
@@ -595,12 +505,11 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
         pf[4 + e] = pv[t >> 1][2 * (t & 1) + 1][e];
       }
 #pragma unroll
-      for (int hb = 0; hb < Tr::HDB; ++hb)
-        dv[hb] = M::mma(swz_kmajor<D>(dob, 0, (db0 + hb) * 32, t, lane), pf, dv[hb]);
+      for (int hb = 0; hb < Tr::HDB; ++hb) dv[hb] = M::mma(crd.read(dob, t, db0 + hb), pf, dv[hb]);
     }
     __syncthreads();  // (C) dS is in LDS
 
-    // Phase 3: role 0 reads dS back; both roles accumulate their half of dK; every wave one block of dQ.
+    // Phase 3: role 0 reads dS back; both roles accumulate their half of dK.
     if (role == 0) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
@@ -618,25 +527,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
         sf[4 + e] = sv[t >> 1][2 * (t & 1) + 1][e];
       }
 #pragma unroll
-      for (int hb = 0; hb < Tr::HDB; ++hb)
-        dk[hb] = M::mma(swz_kmajor<D>(qb, 0, (db0 + hb) * 32, t, lane), sf, dk[hb]);
-    }
-    if (has_dq) {
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int t = 0; t < BC / 16; ++t)
-        acc = M::mma(load_kmajor_frag<bf16>(ds_lds, PS, 0, dq_ib * 32, t, lane), kq[t], acc);
-      float* dst = dqg + (size_t)(q0 + dq_ib * 32 + 4 * g) * D + dq_db * 32 + l32;
-      if (q0 + BR <= N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r] * a.scale);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = q0 + dq_ib * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (i < N) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r] * a.scale);
-        }
-      }
+      for (int hb = 0; hb < Tr::HDB; ++hb) dk[hb] = M::mma(crd.read(qb, t, db0 + hb), sf, dk[hb]);
     }
     qt = qt_next;
     buf ^= 1;
@@ -664,78 +555,174 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ 3. dq = accumulator
+// ------------------------------------------------------------------ 2b. dK / dV, float32
 
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ acc, T* __restrict__ dq, long n4) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n4) return;
-  const f32x4 v = *reinterpret_cast<const f32x4*>(acc + 4 * i);
-  if constexpr (sizeof(T) == 2) {
-    bf16x4 w;
+// float32 variant (used by the float32 workload): four waves, wave w owns keys 32 w .. 32 w + 31 and
+// forms S, dP, P, dS and both dK and dV for them; padded row-major tiles, one query tile at a time.
+template <int D>
+struct F32Traits {
+  static constexpr int BC = 128;
+  static constexpr int BR = 32;
+  static constexpr int NT = 256;
+  static constexpr int PITCH = D + 4;
+  static constexpr int NKF = D / 2;
+  static constexpr int NDB = D / 32;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
+  using Tr = F32Traits<D>;
+  using M = MM<float>;
+  constexpr int BC = Tr::BC, BR = Tr::BR, PITCH = Tr::PITCH;
+  __shared__ __attribute__((aligned(16))) float q_lds[BR * PITCH];
+  __shared__ __attribute__((aligned(16))) float do_lds[BR * PITCH];
+  __shared__ __attribute__((aligned(16))) float lse_lds[BR];
+  __shared__ __attribute__((aligned(16))) float dd_lds[BR];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int kt = (int)(blockIdx.x / BH);
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int hm = a.Hm > 1 ? h : 0;
+  const int N = a.N;
+  const int c0 = kt * BC;
+  const int c1 = min(N, c0 + BC);
+  const int j = c0 + wave * 32 + l32;
+
+  const size_t head = (size_t)bh * N * D;
+  const float* __restrict__ qg = static_cast<const float*>(a.q) + head;
+  const float* __restrict__ kg = static_cast<const float*>(a.k) + head;
+  const float* __restrict__ vg = static_cast<const float*>(a.v) + head;
+  const float* __restrict__ dog = static_cast<const float*>(a.dout) + head;
+  const size_t vrow = ((size_t)b * a.Hm + hm) * N;
+  const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
+  const bool has_lt = a.lts != nullptr;
+  const bool has_ut = a.uts != nullptr;
+  const bool causal = a.causal != 0;
+
+  int m_lts = 0, m_lte = 0, m_uts = 0, m_ute = 0;
+  float kf[Tr::NKF], vf[Tr::NKF];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (bf16)v[e];
-    *reinterpret_cast<bf16x4*>(dq + 4 * i) = w;
-  } else {
-    *reinterpret_cast<f32x4*>(dq + 4 * i) = v;
+  for (int c = 0; c < Tr::NKF; ++c) {
+    kf[c] = j < N ? kg[(size_t)j * D + 2 * c + g] : 0.f;
+    vf[c] = j < N ? vg[(size_t)j * D + 2 * c + g] : 0.f;
+  }
+  if (j < N) {
+    if (has_lt) { m_lts = a.lts[vrow + j]; m_lte = a.lte[vrow + j]; }
+    if (has_ut) { m_uts = a.uts[vrow + j]; m_ute = a.ute[vrow + j]; }
+  }
+
+  f32x16 dk[Tr::NDB], dv[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+  int bnd[8];
+  merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N, bnd);
+  const int nq = (N + BR - 1) / BR;
+  for (int qt = causal ? c0 / BR : 0; qt < nq; ++qt) {
+    const int q0 = qt * BR;
+    const int q1 = min(N, q0 + BR);
+    const int cls = classify_tile(q0, q1, c0, c1, bnd, causal);
+    if (cls == CLS_FULL) continue;
+    const bool need_mask = (cls == CLS_PARTIAL) || (q1 - q0 < BR) || (c1 - c0 < BC);
+    __syncthreads();
+    load_tile<float, BR, D, PITCH, Tr::NT>(q_lds, qg, q0, N, tid);
+    load_tile<float, BR, D, PITCH, Tr::NT>(do_lds, dog, q0, N, tid);
+    if (tid < BR) {
+      const int i = q0 + tid;
+      const float l = i < N ? a.lse[(size_t)bh * N + i] : INFINITY;
+      lse_lds[tid] = ((l == -INFINITY) ? INFINITY : l) * LOG2E;
+      dd_lds[tid] = i < N ? a.dd[(size_t)bh * N + i] : 0.f;
+    }
+    __syncthreads();
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int c = 0; c < Tr::NKF; ++c) {
+      s = M::mma(q_lds[l32 * PITCH + 2 * c + g], kf[c], s);
+      dp = M::mma(do_lds[l32 * PITCH + 2 * c + g], vf[c], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int il = 8 * (r >> 2) + 4 * g + (r & 3);
+      const int i = q0 + il;
+      float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - lse_lds[il]);
+      const bool msk = need_mask &
+                       ((i >= N) | (j >= N) | masked_elem(i, j, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute));
+      p = msk ? 0.f : p;
+      s[r] = p;
+      dp[r] = p * (dp[r] - dd_lds[il]);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        dv[db] = M::mma(load_kmajor_frag<float>(do_lds, PITCH, 0, db * 32, t, lane), s[t], dv[db]);
+        dk[db] = M::mma(load_kmajor_frag<float>(q_lds, PITCH, 0, db * 32, t, lane), dp[t], dk[db]);
+      }
+    }
+  }
+  if (j < N) {
+    float* dkg = static_cast<float*>(a.dk) + head + (size_t)j * D;
+    float* dvg = static_cast<float*>(a.dv) + head + (size_t)j * D;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * g;
+        f32x4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = dk[db][4 * q4 + e] * a.scale;
+          wv[e] = dv[db][4 * q4 + e];
+        }
+        *reinterpret_cast<f32x4*>(dkg + d0) = wk;
+        *reinterpret_cast<f32x4*>(dvg + d0) = wv;
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------------ host launch
 
 template <typename T, int D>
-static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                               const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* dd,
-                               const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds,
-                               int B, int H, int N, int Hm, int causal, float scale, hipStream_t stream) {
-  const long rows = (long)B * H * N;
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int RPB = 256 / CPR;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                     static_cast<const T*>(out), static_cast<const T*>(dout), dd, dq_acc, rows);
+static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
+  const long nq = (a.N + DqTraits<T, D>::BR - 1) / DqTraits<T, D>::BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)(nq * a.B * a.H)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-
-  BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.dd = dd; a.dq_acc = dq_acc; a.dk = dk; a.dv = dv;
-  a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
-  a.B = B; a.H = H; a.N = N; a.Hm = Hm;
-  a.nkt = (N + BwdTraits<T, D>::BC - 1) / BwdTraits<T, D>::BC;
-  a.nkb = (N + KBLOCK - 1) / KBLOCK;
-  a.causal = causal;
-  a.scale = scale;
-  a.scale_log2 = scale * LOG2E;
-  const long grid = (long)a.nkt * B * H;
+  const long nkt = (a.N + 127) / 128;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((bwd_pair_kernel<D>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)(nkt * a.B * a.H)), dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((unsigned)(nkt * a.B * a.H)), dim3(256), 0, stream, a);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const long n4 = rows * D / 4;
-  hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, dq_acc,
-                     static_cast<T*>(dq), n4);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
-                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* dd,
-                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B,
-                      int H, int N, int Hm, int causal, float scale, hipStream_t stream) {
-  if (bf16_in) {
-    if (d == 64)
-      return launch_bwd_t<bf16, 64>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
-                                    N, Hm, causal, scale, stream);
-    return launch_bwd_t<bf16, 128>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
-                                   N, Hm, causal, scale, stream);
-  }
-  if (d == 64)
-    return launch_bwd_t<float, 64>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
-                                   N, Hm, causal, scale, stream);
-  return launch_bwd_t<float, 128>(q, k, v, out, dout, lse, dq, dk, dv, dq_acc, dd, lts, lte, uts, ute, bounds, B, H,
-                                  N, Hm, causal, scale, stream);
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
+                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int N, int Hm,
+                      int causal, float scale, hipStream_t stream) {
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.dd = dd;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
+  a.B = B; a.H = H; a.N = N; a.Hm = Hm;
+  a.nkb = (N + KBLOCK - 1) / KBLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * LOG2E;
+  if (bf16_in) return d == 64 ? launch_bwd_t<bf16, 64>(a, stream) : launch_bwd_t<bf16, 128>(a, stream);
+  return d == 64 ? launch_bwd_t<float, 64>(a, stream) : launch_bwd_t<float, 128>(a, stream);
 }
 
 }  // namespace fm

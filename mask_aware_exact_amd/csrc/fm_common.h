@@ -258,6 +258,47 @@ __device__ __forceinline__ bf16x8 swz_kmajor(const bf16* tile, int row0, int col
   return f;
 }
 
+// Precomputed per-lane byte offsets for the two read patterns of a swizzled tile. Because swz_key
+// depends only on the low four row bits, moving by 32 rows (row reads) or 16 rows (transposing reads)
+// keeps every offset, so the loops add compile-time row strides to a handful of lane constants.
+template <int D>
+struct SwzRowReads {  // operand with k along the row: lane reads row rb * 32 + lane % 32, chunk 2 c + lane / 32
+  int off[D / 16];
+  __device__ __forceinline__ void init(int lane) {
+    const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) off[c] = swz_off<D>(r, c * 16 + g * 8);
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* tile, int rb, int c) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + rb * 32 * (D * 2) + off[c]);
+  }
+};
+
+template <int D>
+struct SwzColReads {  // operand with k along the rows (the load_kmajor_frag pattern), one 32-column block db
+  int lo[D / 32], hi[D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, s = lane & 15;
+    const int row = 4 * g + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + (lane & 16) + 4 * (s & 3);
+      lo[db] = swz_off<D>(row, col);
+      hi[db] = swz_off<D>(row + 8, col);
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* tile, int t, int db) const {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const char* base = reinterpret_cast<const char*>(tile) + t * 16 * (D * 2);
+    const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + lo[db]));
+    const bf16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + hi[db]));
+    bf16x8 f;
+    f[0] = x[0]; f[1] = x[1]; f[2] = x[2]; f[3] = x[3];
+    f[4] = y[0]; f[5] = y[1]; f[6] = y[2]; f[7] = y[3];
+    return f;
+  }
+};
+
 // 16-byte global/LDS copy helpers.
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }

@@ -39,7 +39,7 @@ def test_size_queries(lib):
     assert lib.fm_bounds_elems(2, 3, 130) == 2 * 3 * 3 * 8
     assert lib.fm_bounds_elems(0, 1, 10) == 0 and lib.fm_bounds_elems(1, 1, (1 << 24) + 1) == 0
     n = lib.fm_bwd_workspace_bytes(fm.FM_BF16, 1, 2, 100, 64)
-    assert n >= 1 * 2 * 100 * 64 * 4 + 1 * 2 * 100 * 4 and n % 256 == 0
+    assert n >= 1 * 2 * 100 * 4 and n % 256 == 0
     assert lib.fm_bwd_workspace_bytes(fm.FM_BF16, 1, 2, 100, 96) == 0
     assert lib.fm_bwd_workspace_bytes(7, 1, 2, 100, 64) == 0
 
