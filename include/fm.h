@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   FM_OK = 0,
   FM_ERR_INVALID = 1,     /* NULL required pointer, B/H/N out of range, Hm not in {1, H}, half-NULL pair,
-                             non-finite scale, vectors without bounds, qblock not positive */
+                             scale not finite and positive, vectors without bounds, qblock not positive */
   FM_ERR_UNSUPPORTED = 2, /* d not in {64, 128} or unknown dtype */
   FM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fm_bwd_workspace_bytes() */
   FM_ERR_LAUNCH = 4       /* the HIP runtime reported an error for a launch */
@@ -81,6 +81,7 @@ fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* 
  *   out[b,h,i,:] = sum_j P_ij v[b,h,j,:],  P_ij = exp(S_ij - lse_i) on unmasked (i, j), 0 elsewhere,
  *   S_ij = scale * q[b,h,i,:] . k[b,h,j,:],  lse[b,h,i] = log(sum over unmasked j of exp(S_ij)).
  * Vectors for head h are read at [b, (Hm == H ? h : 0), :]. causal != 0 adds the i < j mask.
+ * scale must be finite and positive (the usual 1 / sqrt(d)).
  * bf16 inputs use bf16 matrix products with float32 accumulation and a float32 softmax; out is
  * rounded to bf16 (nearest even). float32 inputs use float32 matrix products.
  * Errors: FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_LAUNCH. */

@@ -78,7 +78,7 @@ fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, in
                  const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
                  const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return FM_ERR_INVALID;
-  if (!sizes_ok(B, H, N) || !std::isfinite(scale)) return FM_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
   fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
   if (st != FM_OK) return st;
   st = dtype_d_ok(dtype, d);
@@ -101,7 +101,7 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return FM_ERR_INVALID;
-  if (!sizes_ok(B, H, N) || !std::isfinite(scale)) return FM_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
   fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
   if (st != FM_OK) return st;
   st = dtype_d_ok(dtype, d);

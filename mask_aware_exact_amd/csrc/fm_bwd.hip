@@ -46,9 +46,9 @@ struct DqTraits {
   static constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
   static constexpr int BC = 64;   // keys per tile (one bounds entry)
   static constexpr int NT = 256;
-  static constexpr bool SWZ = sizeof(T) == 2;            // bf16 K tile: swizzled, unpadded
-  static constexpr int KP = SWZ ? D : D + 4;             // K row pitch (elements)
-  static constexpr int VP = D + 16 / (int)sizeof(T);     // V row pitch: 16-byte padding (row reads only)
+  static constexpr bool SWZ = sizeof(T) == 2;            // bf16 K and V tiles: swizzled, unpadded
+  static constexpr int KP = SWZ ? D : D + 4;             // row pitch (elements)
+  static constexpr int VP = KP;
   static constexpr int NQF = D / MM<T>::KW;
   static constexpr int NDB = D / 32;
   static constexpr int TPB = 16 / MM<T>::E;
@@ -140,18 +140,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int nkt = (N + BC - 1) / BC;
   const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
 
-  i32x4 kr[CH], vr[CH];
+  // Next tile: K / V (bf16: straight into LDS buffer `dst`; float: into staging registers) and the
+  // tile's mask vectors (registers).
+  constexpr int CHR = SWZ ? 1 : CH;
+  i32x4 kr[CHR], vr[CHR];
   i32x4 mr = {0, 0, 0, 0};
-  auto fetch = [&](int kt) {
+  auto fetch = [&](int kt, int dst) {
     const int c0 = kt * BC;
+    if constexpr (SWZ) {
+      copy_tile_async<D, BC, 4>(reinterpret_cast<bf16*>(k_lds[dst]), reinterpret_cast<const bf16*>(kg), c0, N, wave,
+                                lane);
+      copy_tile_async<D, BC, 4>(reinterpret_cast<bf16*>(v_lds[dst]), reinterpret_cast<const bf16*>(vg), c0, N, wave,
+                                lane);
+    } else {
 #pragma unroll
-    for (int it = 0; it < CH; ++it) {
-      const int c = it * Tr::NT + tid;
-      const int r = c / CPR, cc = c % CPR;
-      const bool ok = c0 + r < N;
-      const size_t rr = ok ? (size_t)(c0 + r) : 0;
-      kr[it] = ld16(reinterpret_cast<const char*>(kg + rr * D) + cc * 16);
-      vr[it] = ld16(reinterpret_cast<const char*>(vg + rr * D) + cc * 16);
+      for (int it = 0; it < CH; ++it) {
+        const int c = it * Tr::NT + tid;
+        const int r = c / CPR, cc = c % CPR;
+        const size_t rr = (size_t)min(c0 + r, N - 1);
+        kr[it] = ld16(reinterpret_cast<const char*>(kg + rr * D) + cc * 16);
+        vr[it] = ld16(reinterpret_cast<const char*>(vg + rr * D) + cc * 16);
+      }
     }
     if (tid < BC) {
       const int j = c0 + tid;
@@ -163,16 +172,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   };
   auto stash = [&](int buf) {
+    if constexpr (!SWZ) {
 #pragma unroll
-    for (int it = 0; it < CH; ++it) {
-      const int c = it * Tr::NT + tid;
-      const int r = c / CPR, cc = c % CPR;
-      if constexpr (SWZ) {
-        st16(reinterpret_cast<char*>(k_lds[buf]) + swz_off<D>(r, cc * 8), kr[it]);
-      } else {
+      for (int it = 0; it < CH; ++it) {
+        const int c = it * Tr::NT + tid;
+        const int r = c / CPR, cc = c % CPR;
         st16(reinterpret_cast<char*>(&k_lds[buf][r * KP]) + cc * 16, kr[it]);
+        st16(reinterpret_cast<char*>(&v_lds[buf][r * VP]) + cc * 16, vr[it]);
       }
-      st16(reinterpret_cast<char*>(&v_lds[buf][r * VP]) + cc * 16, vr[it]);
     }
     if (tid < BC) vec_lds[buf][tid] = mr;
   };
@@ -184,36 +191,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   TileWindow win = empty_window();
   int kt = next_live_tile(win, 0, kt_end, class_of, lane);
-  if (kt < kt_end) fetch(kt);
+  if (kt < kt_end) fetch(kt, 0);
   int buf = 0;
 
   while (kt < kt_end) {
     const int c0 = kt * BC;
     const bool need_mask = window_partial(win, kt) || (c0 + BC > N);
     stash(buf);
+    if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();
     const int kt_next = next_live_tile(win, kt + 1, kt_end, class_of, lane);
-    if (kt_next < kt_end) fetch(kt_next);
+    if (kt_next < kt_end) fetch(kt_next, buf ^ 1);
 
     const T* kt_lds = k_lds[buf];
     const T* vt_lds = v_lds[buf];
-    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks (rows = keys, columns = queries).
+    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks (rows = keys, columns = queries). Product
+    // blocks run at raised wave priority, so the two waves of a SIMD drift into opposite phases.
+    __builtin_amdgcn_s_setprio(2);
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       s[jb] = zero16();
       dp[jb] = zero16();
-      const T* vrow_l = vt_lds + (jb * 32 + l32) * VP + g * M::E;
 #pragma unroll
       for (int c = 0; c < Tr::NQF; ++c) {
         if constexpr (SWZ) {
           s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
+          dp[jb] = M::mma(krd.read(vt_lds, jb, c), df[c], dp[jb]);
         } else {
           s[jb] = M::mma(load_kcontig_frag<T>(kt_lds + (jb * 32 + l32) * KP + g * M::E + c * M::KW), qf[c], s[jb]);
+          dp[jb] = M::mma(load_kcontig_frag<T>(vt_lds + (jb * 32 + l32) * VP + g * M::E + c * M::KW), df[c], dp[jb]);
         }
-        dp[jb] = M::mma(load_kcontig_frag<T>(vrow_l + c * M::KW), df[c], dp[jb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0.
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
@@ -235,6 +246,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     // dQ^T += K^T dS^T over the 64 keys of the tile.
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int t = 0; t < 2 * Tr::TPB; ++t) {
       const typename M::frag sf = acc_frag<T>(dp[t / Tr::TPB], t % Tr::TPB);
@@ -247,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     kt = kt_next;
     buf ^= 1;
   }
@@ -288,7 +301,8 @@ struct PairTraits {
   static constexpr int BC = 128;          // keys per workgroup
   static constexpr int BR = 64;           // query rows per iteration
   static constexpr int NT = 512;
-  static constexpr int PS = BR + 8;       // P and dS tiles [key][row]
+  static constexpr int PS = BR + 4;       // P and dS tiles [key][row]: a 34-dword pitch gives the 32 rows of
+                                          // one 8-byte access 32 distinct bank pairs
   static constexpr int NKF = D / 16;      // K or V fragments per lane (k = d)
   static constexpr int NDB = D / 32;      // 32-wide d blocks
   static constexpr int HDB = NDB / 2;     // d blocks per role
@@ -437,6 +451,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     const bf16* xb = role == 0 ? qb : dob;
 
     // Phase 1: role 0 forms S and P, role 1 forms dP (rows = query rows, columns = this lane's keys).
+    __builtin_amdgcn_s_setprio(2);
     f32x16 x[2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
@@ -444,6 +459,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(xb, ib, c), xf[c], x[ib]);
     }
+    __builtin_amdgcn_s_setprio(0);
     bf16x4 pv[2][4];  // P (role 0: computed, role 1: read back), register order
     if (role == 0) {
       if (need_mask) {

@@ -299,6 +299,31 @@ struct SwzColReads {  // operand with k along the rows (the load_kmajor_frag pat
   }
 };
 
+// Asynchronous copy of rows [row0, row0 + ROWS) of a [*, D] bf16 matrix into a swizzled LDS tile with
+// direct global-to-LDS loads: each wave instruction moves 1 KB (16 bytes per lane, written lane-linearly
+// at the instruction's LDS address), and lane l of the instruction fetches the global chunk that the
+// swizzle places at its position. Rows at or past nrows read row nrows - 1 (finite data the kernels
+// mask). NW waves take part. The caller waits with s_waitcnt vmcnt(0) and a barrier before reading.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void copy_tile_async(bf16* tile, const bf16* __restrict__ g, int row0, int nrows,
+                                                int wave, int lane) {
+  constexpr int RB = D * 2;        // bytes per row
+  constexpr int RPI = 1024 / RB;   // rows per instruction
+  constexpr int NI = ROWS / RPI;   // instructions per tile
+  constexpr int CPW = RB / 16;     // 16-byte chunks per row
+  static_assert(ROWS % RPI == 0 && NI % NW == 0, "the tile must split evenly over the waves");
+  const int rl = lane / CPW, pos = lane % CPW;
+#pragma unroll
+  for (int k = 0; k < NI / NW; ++k) {
+    const int i = __builtin_amdgcn_readfirstlane(wave + k * NW);
+    const int r = i * RPI + rl;
+    const int gr = min(row0 + r, nrows - 1);
+    const bf16* src = g + (size_t)gr * D + ((pos ^ swz_key<D>(r)) << 3);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(tile) + i * 1024),
+                                     16, 0, 0);
+  }
+}
+
 // 16-byte global/LDS copy helpers.
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }

@@ -11,9 +11,9 @@
 //    the other's matrix products.
 //  * key tiles of BC = 64 columns (one bounds entry). The live (not fully masked) tiles are found 64 at
 //    a time with one wave-wide ballot; the next live tile is fetched from HBM into registers while the
-//    current one is computed, and K / V are double-buffered in LDS. K rows are padded by 16 bytes
-//    (32 lanes reading one 16-byte chunk of 32 rows hit distinct banks); V rows by 64 bytes (the four
-//    rows of one transposing read start 16 banks apart).
+//    current one is computed, and K / V are double-buffered in LDS. For bf16 the tiles are unpadded with
+//    an XOR chunk swizzle (conflict-free for the row reads of K and the transposing reads of V) and are
+//    filled by direct global-to-LDS copies, so no registers stage them.
 //  * each wave computes S^T = K Q^T (keys as the M axis, its 32 queries as the N axis), so every lane
 //    holds one query row and the row max needs one exchange with lane ^ 32; the row sum stays split
 //    across the two lanes until the epilogue.
@@ -68,8 +68,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   constexpr int BR = Tr::BR, BC = Tr::BC, PITCH = Tr::PITCH, CPR = Tr::CPR, CH = Tr::CH;
   constexpr int VPITCH = Tr::VPITCH;
-  __shared__ __attribute__((aligned(16))) T k_lds[2][BC * PITCH];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VPITCH];
+  // bf16: K and V tiles are swizzled and unpadded, filled by direct global-to-LDS copies (no staging
+  // registers). float: padded row-major tiles staged through registers.
+  constexpr bool SWZ = sizeof(T) == 2;
+  constexpr int KLP = SWZ ? D : PITCH;
+  constexpr int VLP = SWZ ? D : VPITCH;
+  __shared__ __attribute__((aligned(16))) T k_lds[2][BC * KLP];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VLP];
   __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
 
   const int tid = threadIdx.x;
@@ -120,20 +125,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int nkt = (N + BC - 1) / BC;
   const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
 
-  // Prefetch registers for one K / V tile and its mask vectors.
-  i32x4 kr[CH], vr[CH];
+  // Next tile: K / V (bf16: straight into LDS buffer `dst`; float: into staging registers) and the
+  // tile's mask vectors (registers).
+  constexpr int CHR = SWZ ? 1 : CH;
+  i32x4 kr[CHR], vr[CHR];
   i32x4 mr = {0, 0, 0, 0};
-  auto fetch = [&](int kt) {
+  auto fetch = [&](int kt, int dst) {
     const int c0 = kt * BC;
+    if constexpr (SWZ) {
+      copy_tile_async<D, BC, 4>(reinterpret_cast<bf16*>(k_lds[dst]), reinterpret_cast<const bf16*>(kg), c0, N, wave,
+                                lane);
+      copy_tile_async<D, BC, 4>(reinterpret_cast<bf16*>(v_lds[dst]), reinterpret_cast<const bf16*>(vg), c0, N, wave,
+                                lane);
+    } else {
 #pragma unroll
-    for (int it = 0; it < CH; ++it) {
-      const int c = it * Tr::NT + tid;
-      const int r = c / CPR, cc = c % CPR;
-      kr[it] = i32x4{0, 0, 0, 0};
-      vr[it] = i32x4{0, 0, 0, 0};
-      if (c0 + r < N) {
-        kr[it] = ld16(reinterpret_cast<const char*>(kg + (size_t)(c0 + r) * D) + cc * 16);
-        vr[it] = ld16(reinterpret_cast<const char*>(vg + (size_t)(c0 + r) * D) + cc * 16);
+      for (int it = 0; it < CH; ++it) {
+        const int c = it * Tr::NT + tid;
+        const int r = c / CPR, cc = c % CPR;
+        const size_t rr = (size_t)min(c0 + r, N - 1);
+        kr[it] = ld16(reinterpret_cast<const char*>(kg + rr * D) + cc * 16);
+        vr[it] = ld16(reinterpret_cast<const char*>(vg + rr * D) + cc * 16);
       }
     }
     if (tid < BC) {
@@ -146,15 +157,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
   };
   auto stash = [&](int buf) {
+    if constexpr (!SWZ) {
 #pragma unroll
-    for (int it = 0; it < CH; ++it) {
-      const int c = it * Tr::NT + tid;
-      const int r = c / CPR, cc = c % CPR;
-      st16(reinterpret_cast<char*>(&k_lds[buf][r * PITCH]) + cc * 16, kr[it]);
-      st16(reinterpret_cast<char*>(&v_lds[buf][r * VPITCH]) + cc * 16, vr[it]);
+      for (int it = 0; it < CH; ++it) {
+        const int c = it * Tr::NT + tid;
+        const int r = c / CPR, cc = c % CPR;
+        st16(reinterpret_cast<char*>(&k_lds[buf][r * PITCH]) + cc * 16, kr[it]);
+        st16(reinterpret_cast<char*>(&v_lds[buf][r * VPITCH]) + cc * 16, vr[it]);
+      }
     }
     if (tid < BC) vec_lds[buf][tid] = mr;
   };
+  SwzRowReads<D> krd;
+  SwzColReads<D> vcd;
+  if constexpr (SWZ) {
+    krd.init(lane);
+    vcd.init(lane);
+  }
 
   auto class_of = [&](int t) {
     int bt[8];
@@ -163,29 +182,40 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   };
   TileWindow win = empty_window();
   int kt = next_live_tile(win, 0, kt_end, class_of, lane);
-  if (kt < kt_end) fetch(kt);
+  if (kt < kt_end) fetch(kt, 0);
   int buf = 0;
 
   while (kt < kt_end) {
     const int c0 = kt * BC;
     const bool need_mask = window_partial(win, kt) || (c0 + BC > N);
     stash(buf);
+    if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();
     const int kt_next = next_live_tile(win, kt + 1, kt_end, class_of, lane);
-    if (kt_next < kt_end) fetch(kt_next);
+    if (kt_next < kt_end) fetch(kt_next, buf ^ 1);
 
     const T* kt_lds = k_lds[buf];
     const T* vt_lds = v_lds[buf];
-    // S^T for the two 32-key blocks: rows = keys, columns = this wave's queries.
+    // S^T for the two 32-key blocks: rows = keys, columns = this wave's queries. Matrix-product blocks
+    // run at raised wave priority so that the two waves of a SIMD drift into opposite phases (one in
+    // products, one in softmax arithmetic).
+    __builtin_amdgcn_s_setprio(2);
     f32x16 s[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       s[jb] = zero16();
-      const T* krow = kt_lds + (jb * 32 + l32) * PITCH + g * M::E;
+      if constexpr (SWZ) {
 #pragma unroll
-      for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(load_kcontig_frag<T>(krow + c * M::KW), qf[c], s[jb]);
+        for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
+      } else {
+        const T* krow = kt_lds + (jb * 32 + l32) * PITCH + g * M::E;
+#pragma unroll
+        for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(load_kcontig_frag<T>(krow + c * M::KW), qf[c], s[jb]);
+      }
     }
 
+    __builtin_amdgcn_s_setprio(0);
+    // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
     float mx = -INFINITY;
     if (need_mask) {
 #pragma unroll
@@ -198,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const int j = c0 + jl;
             const i32x4 mv = vec_lds[buf][jl];
             const bool msk = (j >= N) | masked_elem(row, j, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
-            const float x = msk ? -INFINITY : s[jb][4 * q4 + e] * sl2;
+            const float x = msk ? -INFINITY : s[jb][4 * q4 + e];
             s[jb][4 * q4 + e] = x;
             mx = fmaxf(mx, x);
           }
@@ -208,14 +238,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = s[jb][r] * sl2;
-          s[jb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
     // Raise the reference only when some row of the wave would exceed it by more than the threshold.
     const bool grow = mx > m_ref + RESCALE_THRESHOLD;
     if (__ballot(grow) != 0) {
@@ -235,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[jb][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], sl2, -m_use));
         s[jb][r] = p;
         psum += p;
       }
@@ -243,14 +269,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     l_run += psum;
 
     // O^T += V^T P^T over the 64 keys of the tile.
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int t = 0; t < 2 * Tr::TPB; ++t) {
       const typename M::frag pf = acc_frag<T>(s[t / Tr::TPB], t % Tr::TPB);
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
-        o[db] = M::mma(load_kmajor_frag<T>(vt_lds, VPITCH, 0, db * 32, t, lane), pf, o[db]);
+        if constexpr (SWZ) {
+          o[db] = M::mma(vcd.read(vt_lds, t, db), pf, o[db]);
+        } else {
+          o[db] = M::mma(load_kmajor_frag<T>(vt_lds, VPITCH, 0, db * 32, t, lane), pf, o[db]);
+        }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     kt = kt_next;
     buf ^= 1;
   }

@@ -73,6 +73,8 @@ def test_fwd_validation(lib):
     assert _fwd(lib, N=(1 << 24) + 1) == fm.FM_ERR_INVALID
     assert _fwd(lib, scale=float("inf")) == fm.FM_ERR_INVALID
     assert _fwd(lib, scale=float("nan")) == fm.FM_ERR_INVALID
+    assert _fwd(lib, scale=0.0) == fm.FM_ERR_INVALID
+    assert _fwd(lib, scale=-0.5) == fm.FM_ERR_INVALID
     assert _fwd(lib, lts=A) == fm.FM_ERR_INVALID                      # half-NULL pair
     assert _fwd(lib, ute=A) == fm.FM_ERR_INVALID
     assert _fwd(lib, lts=A, lte=A) == fm.FM_ERR_INVALID               # vectors without bounds
@@ -98,6 +100,7 @@ def test_bwd_validation(lib):
     for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"):
         assert _bwd(lib, **{name: None}) == fm.FM_ERR_INVALID, name
     assert _bwd(lib, H=0) == fm.FM_ERR_INVALID
+    assert _bwd(lib, scale=-1.0) == fm.FM_ERR_INVALID
     assert _bwd(lib, uts=A) == fm.FM_ERR_INVALID
     assert _bwd(lib, uts=A, ute=A) == fm.FM_ERR_INVALID
     assert _bwd(lib, d=32) == fm.FM_ERR_UNSUPPORTED
