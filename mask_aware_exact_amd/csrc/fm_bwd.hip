@@ -301,8 +301,6 @@ struct PairTraits {
   static constexpr int BC = 128;          // keys per workgroup
   static constexpr int BR = 64;           // query rows per iteration
   static constexpr int NT = 512;
-  static constexpr int PS = BR + 4;       // P and dS tiles [key][row]: a 34-dword pitch gives the 32 rows of
-                                          // one 8-byte access 32 distinct bank pairs
   static constexpr int NKF = D / 16;      // K or V fragments per lane (k = d)
   static constexpr int NDB = D / 32;      // 32-wide d blocks
   static constexpr int HDB = NDB / 2;     // d blocks per role
@@ -315,12 +313,14 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Tr = PairTraits<D>;
   using M = MM<bf16>;
-  constexpr int BC = Tr::BC, BR = Tr::BR, PS = Tr::PS, CPR = Tr::CPR, CH = Tr::CH;
+  constexpr int BC = Tr::BC, BR = Tr::BR, CPR = Tr::CPR, CH = Tr::CH;
   // Q and dO tiles are swizzled and unpadded (rows of D elements), two of each (double buffer).
   __shared__ __attribute__((aligned(16))) bf16 q_lds[2 * BR * D];
   __shared__ __attribute__((aligned(16))) bf16 do_lds[2 * BR * D];
-  __shared__ __attribute__((aligned(16))) bf16 p_lds[BC * PS];
-  __shared__ __attribute__((aligned(16))) bf16 ds_lds[BC * PS];
+  // P and dS pass between the two waves of a key group in register order, lane-interleaved: chunk k
+  // (4 values) of lane l sits at [group][k][l], so every 8-byte access of a wave is 512 contiguous bytes.
+  __shared__ __attribute__((aligned(16))) bf16x4 p_xch[4][8][64];
+  __shared__ __attribute__((aligned(16))) bf16x4 s_xch[4][8][64];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BR];
   __shared__ __attribute__((aligned(16))) float dd_lds[2][BR];
 
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
               const float p = __builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
               pv[ib][q4][e] = (bf16)(((mw >> (8 * q4 + e)) & 1u) ? 0.f : p);
             }
-            *reinterpret_cast<bf16x4*>(p_lds + jl * PS + il0) = pv[ib][q4];
+            p_xch[kgrp][4 * ib + q4][lane] = pv[ib][q4];
           }
         }
       } else {
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
             const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) pv[ib][q4][e] = (bf16)__builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
-            *reinterpret_cast<bf16x4*>(p_lds + jl * PS + il0) = pv[ib][q4];
+            p_xch[kgrp][4 * ib + q4][lane] = pv[ib][q4];
           }
         }
       }
@@ -504,11 +504,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int il0 = ib * 32 + 8 * q4 + 4 * g;
-          pv[ib][q4] = *reinterpret_cast<const bf16x4*>(p_lds + jl * PS + il0);
+          pv[ib][q4] = p_xch[kgrp][4 * ib + q4][lane];
           const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[buf][il0]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)pv[ib][q4][e] * (x[ib][4 * q4 + e] - dd4[e]));
-          *reinterpret_cast<bf16x4*>(ds_lds + jl * PS + il0) = sv[ib][q4];
+          s_xch[kgrp][4 * ib + q4][lane] = sv[ib][q4];
         }
       }
     }
@@ -530,8 +530,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          sv[ib][q4] = *reinterpret_cast<const bf16x4*>(ds_lds + jl * PS + ib * 32 + 8 * q4 + 4 * g);
+        for (int q4 = 0; q4 < 4; ++q4) sv[ib][q4] = s_xch[kgrp][4 * ib + q4][lane];
       }
     }
 #pragma unroll
