@@ -67,8 +67,7 @@ __global__ __launch_bounds__(256) void tile_classes_kernel(const int* __restrict
   const int kt = (int)(idx % nkt);
   const int qt = (int)((idx / nkt) % nq);
   const int row = (int)(idx / ((long)nkt * nq));
-  int b[8];
-  merged_bounds(bounds == nullptr ? nullptr : bounds + (size_t)row * nkt * 8, kt, kt + 1, N, b);
+  const TileBounds b = merged_bounds(bounds == nullptr ? nullptr : bounds + (size_t)row * nkt * 8, kt, kt + 1, N);
   const int r0 = qt * qblock, r1 = min(N, r0 + qblock);
   const int c0 = kt * KBLOCK, c1 = min(N, c0 + KBLOCK);
   classes[idx] = (uint8_t)classify_tile(r0, r1, c0, c1, b, causal != 0);

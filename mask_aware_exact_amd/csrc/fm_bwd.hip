@@ -185,8 +185,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   auto class_of = [&](int t) {
-    int bt[8];
-    merged_bounds(brow, t, t + 1, N, bt);
+    const TileBounds bt = merged_bounds(brow, t, t + 1, N);
     return classify_tile(r0, r1, t * BC, min(N, t * BC + BC), bt, causal);
   };
   TileWindow win = empty_window();
@@ -374,9 +373,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     }
   }
   SwzRowReads<D> rrd;
-  SwzColReads<D> crd;
+  SwzColReads<D, Tr::HDB> crd;
   rrd.init(lane);
-  crd.init(lane);
+  crd.init(lane, role * Tr::HDB);
 
   f32x16 dk[Tr::HDB], dv[Tr::HDB];
 #pragma unroll
@@ -386,8 +385,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   }
   const int db0 = role * Tr::HDB;  // first d block of this role
 
-  int bnd[8];
-  merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N, bnd);
+  const TileBounds bnd = merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N);
   const int nq = (N + BR - 1) / BR;
   const int qt_begin = causal ? c0 / BR : 0;
   auto class_of = [&](int qt) { return classify_tile(qt * BR, min(N, qt * BR + BR), c0, c1, bnd, causal); };
@@ -521,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         pf[4 + e] = pv[t >> 1][2 * (t & 1) + 1][e];
       }
 #pragma unroll
-      for (int hb = 0; hb < Tr::HDB; ++hb) dv[hb] = M::mma(crd.read(dob, t, db0 + hb), pf, dv[hb]);
+      for (int hb = 0; hb < Tr::HDB; ++hb) dv[hb] = M::mma(crd.read(dob, t, hb), pf, dv[hb]);
     }
     __syncthreads();  // (C) dS is in LDS
 
@@ -542,7 +540,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         sf[4 + e] = sv[t >> 1][2 * (t & 1) + 1][e];
       }
 #pragma unroll
-      for (int hb = 0; hb < Tr::HDB; ++hb) dk[hb] = M::mma(crd.read(qb, t, db0 + hb), sf, dk[hb]);
+      for (int hb = 0; hb < Tr::HDB; ++hb) dk[hb] = M::mma(crd.read(qb, t, hb), sf, dk[hb]);
     }
     qt = qt_next;
     buf ^= 1;
@@ -640,8 +638,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
     dk[db] = zero16();
     dv[db] = zero16();
   }
-  int bnd[8];
-  merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N, bnd);
+  const TileBounds bnd = merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N);
   const int nq = (N + BR - 1) / BR;
   for (int qt = causal ? c0 / BR : 0; qt < nq; ++qt) {
     const int q0 = qt * BR;

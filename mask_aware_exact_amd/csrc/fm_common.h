@@ -30,15 +30,21 @@ constexpr float LN2 = 0.6931471805599453f;
 
 enum TileClass : int { CLS_NONE = 0, CLS_PARTIAL = 1, CLS_FULL = 2 };
 
-// Tile rule: rows [r0, r1), columns [c0, c1), both already clipped to N; b = per-tile bounds
-// (mnLTS, mxLTS, mnLTE, mxLTE, mnUTS, mxUTS, mnUTE, mxUTE).
-__device__ __host__ inline int classify_tile(int r0, int r1, int c0, int c1, const int* b, bool causal) {
+// Per-key-tile bounds (min/max of each of LTS, LTE, UTS, UTE over the tile's columns). Named fields
+// rather than an int[8]: a private array that is indexed in a loop may be placed in LDS by the compiler
+// (one 32-byte slot per thread), and every read of it then hits the same few banks.
+struct TileBounds {
+  int lts_min, lts_max, lte_min, lte_max, uts_min, uts_max, ute_min, ute_max;
+};
+
+// Tile rule: rows [r0, r1), columns [c0, c1), both already clipped to N.
+__device__ __host__ inline int classify_tile(int r0, int r1, int c0, int c1, const TileBounds& b, bool causal) {
   const bool causal_full = causal && (r1 - 1 < c0);
   const bool causal_none = !causal || (r0 >= c1 - 1);
-  const bool lt_full = (r0 >= b[1]) && (r1 <= b[2]);
-  const bool lt_none = (r1 <= b[0]) || (r0 >= b[3]);
-  const bool ut_full = (r0 >= b[5]) && (r1 <= b[6]);
-  const bool ut_none = (r1 <= b[4]) || (r0 >= b[7]);
+  const bool lt_full = (r0 >= b.lts_max) && (r1 <= b.lte_min);
+  const bool lt_none = (r1 <= b.lts_min) || (r0 >= b.lte_max);
+  const bool ut_full = (r0 >= b.uts_max) && (r1 <= b.ute_min);
+  const bool ut_none = (r1 <= b.uts_min) || (r0 >= b.ute_max);
   if (causal_full || lt_full || ut_full) return CLS_FULL;
   if (causal_none && lt_none && ut_none) return CLS_NONE;
   return CLS_PARTIAL;
@@ -46,21 +52,27 @@ __device__ __host__ inline int classify_tile(int r0, int r1, int c0, int c1, con
 
 // Bounds of key tiles [kt0, kt1) of one (b, hm) row merged by min/max; canonical empties when the
 // bounds array is absent (all vectors absent).
-__device__ inline void merged_bounds(const int* __restrict__ brow, int kt0, int kt1, int N, int* out) {
+__device__ inline TileBounds merged_bounds(const int* __restrict__ brow, int kt0, int kt1, int N) {
+  TileBounds r;
   if (brow == nullptr) {
-    out[0] = out[1] = out[2] = out[3] = N;
-    out[4] = out[5] = out[6] = out[7] = 0;
-    return;
+    r.lts_min = r.lts_max = r.lte_min = r.lte_max = N;
+    r.uts_min = r.uts_max = r.ute_min = r.ute_max = 0;
+    return r;
   }
   const int* p = brow + (size_t)kt0 * 8;
-  for (int e = 0; e < 8; ++e) out[e] = p[e];
+  r = TileBounds{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
   for (int t = kt0 + 1; t < kt1; ++t) {
     const int* q = brow + (size_t)t * 8;
-    for (int e = 0; e < 8; e += 2) {
-      out[e] = min(out[e], q[e]);
-      out[e + 1] = max(out[e + 1], q[e + 1]);
-    }
+    r.lts_min = min(r.lts_min, q[0]);
+    r.lts_max = max(r.lts_max, q[1]);
+    r.lte_min = min(r.lte_min, q[2]);
+    r.lte_max = max(r.lte_max, q[3]);
+    r.uts_min = min(r.uts_min, q[4]);
+    r.uts_max = max(r.uts_max, q[5]);
+    r.ute_min = min(r.ute_min, q[6]);
+    r.ute_max = max(r.ute_max, q[7]);
   }
+  return r;
 }
 
 // Live-tile window over 64 consecutive tiles: bit t of `live` / `partial` describes tile base + t.
@@ -274,17 +286,20 @@ struct SwzRowReads {  // operand with k along the row: lane reads row rb * 32 + 
   }
 };
 
-template <int D>
+// SwzColReads<D, NB> covers the NB 32-column blocks db_first .. db_first + NB - 1 (db_first may be a run-time
+// value); read() takes the block's index within that range and must be given compile-time indices, so
+// that the offsets stay in registers (a dynamically indexed private array may be placed in LDS).
+template <int D, int NB = D / 32>
 struct SwzColReads {  // operand with k along the rows (the load_kmajor_frag pattern), one 32-column block db
-  int lo[D / 32], hi[D / 32];
-  __device__ __forceinline__ void init(int lane) {
+  int lo[NB], hi[NB];
+  __device__ __forceinline__ void init(int lane, int db_first = 0) {
     const int g = lane >> 5, s = lane & 15;
     const int row = 4 * g + (s >> 2);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = db * 32 + (lane & 16) + 4 * (s & 3);
-      lo[db] = swz_off<D>(row, col);
-      hi[db] = swz_off<D>(row + 8, col);
+    for (int i = 0; i < NB; ++i) {
+      const int col = (db_first + i) * 32 + (lane & 16) + 4 * (s & 3);
+      lo[i] = swz_off<D>(row, col);
+      hi[i] = swz_off<D>(row + 8, col);
     }
   }
   __device__ __forceinline__ bf16x8 read(const bf16* tile, int t, int db) const {

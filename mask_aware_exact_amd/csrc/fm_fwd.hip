@@ -176,8 +176,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   auto class_of = [&](int t) {
-    int bt[8];
-    merged_bounds(brow, t, t + 1, N, bt);
+    const TileBounds bt = merged_bounds(brow, t, t + 1, N);
     return classify_tile(r0, r1, t * BC, min(N, t * BC + BC), bt, causal);
   };
   TileWindow win = empty_window();
