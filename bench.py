@@ -257,7 +257,7 @@ def main():
         "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[1] * 1e-3) / 1e12, 2),
                          "fm_bwd": round(bwd_tflops, 2)},
         "finite_outputs": ok,
-        "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_pre, bwd_pair, bwd_dq launches)",
+        "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_dq_kernel then bwd_dkdv_pair_kernel)",
                      "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(wl.name),
                      "flop_per_call": wl.flop_bwd, "flop_formula": "10*d*U"},
