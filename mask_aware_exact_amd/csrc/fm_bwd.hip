@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T k_lds[2][BC * KP];
   __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VP];
   __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
+  __shared__ __attribute__((aligned(16))) uint32_t cw_lds[4][BC];  // per wave: masked-row words of a tile
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -224,24 +225,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0.
+    // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0 (masked scores set to -inf).
+    if (need_mask) {
+      tile_column_words(cw_lds[wave], vec_lds[buf], r0 + wave * 32, c0, N, causal, has_lt, has_ut, lane);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const i32x4 w4 = column_words4(cw_lds[wave], jb, q4, g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[jb][4 * q4 + e] = select_neg_inf(row_mask_of(w4[e], l32), s[jb][4 * q4 + e]);
+        }
+      }
+    }
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          float p = __builtin_amdgcn_exp2f(s[jb][r] * sl2 - lse2);
-          if (need_mask) {
-            const int jl = jb * 32 + 8 * q4 + 4 * g + e;
-            const i32x4 mv = vec_lds[buf][jl];
-            const bool msk =
-                (c0 + jl >= N) | masked_elem(row, c0 + jl, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
-            p = msk ? 0.f : p;
-          }
-          dp[jb][r] = p * (dp[jb][r] - Di);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[jb][r] * sl2 - lse2);
+        dp[jb][r] = p * (dp[jb][r] - Di);
       }
     }
     // dQ^T += K^T dS^T over the 64 keys of the tile.

@@ -125,9 +125,10 @@ __device__ __forceinline__ bool masked_elem(int i, int j, bool causal, bool has_
 
 // Bits of the query rows [s, e) that fall in [q0, q0 + 64), bit k standing for row q0 + k.
 __device__ __forceinline__ uint64_t row_span_bits(int s, int e, int q0) {
-  const int a = max(s - q0, 0);
-  const int z = min(e - q0, 64);
-  const uint64_t below_z = z >= 64 ? ~0ull : (z <= 0 ? 0ull : (1ull << z) - 1);
+  // s and e are clamped into [q0, q0 + 64] before any difference, so no vector value can overflow it
+  const int a = min(max(s, q0), q0 + 64) - q0;
+  const int z = min(max(e, q0), q0 + 64) - q0;
+  const uint64_t below_z = z >= 64 ? ~0ull : (1ull << z) - 1;
   const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1;
   return below_z & ~below_a;
 }
@@ -140,6 +141,53 @@ __device__ __forceinline__ uint64_t masked_row_bits(int q0, int j, int N, bool c
   m |= has_lt ? row_span_bits(lts, lte, q0) : 0ull;
   m |= has_ut ? row_span_bits(uts, ute, q0) : 0ull;
   return j >= N ? ~0ull : m;
+}
+
+// The same for the 32 rows q0 .. q0 + 31.
+__device__ __forceinline__ uint32_t row_span_bits32(int s, int e, int q0) {
+  const int a = min(max(s, q0), q0 + 32) - q0;
+  const int z = min(max(e, q0), q0 + 32) - q0;
+  const uint32_t below_z = z >= 32 ? ~0u : (1u << z) - 1;
+  const uint32_t below_a = a >= 32 ? ~0u : (1u << a) - 1;
+  return below_z & ~below_a;
+}
+
+__device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int N, bool causal, bool has_lt, bool has_ut,
+                                                      int lts, int lte, int uts, int ute) {
+  uint32_t m = row_span_bits32(N, 0x7fffffff, q0);
+  m |= causal ? row_span_bits32(0, j, q0) : 0u;
+  m |= has_lt ? row_span_bits32(lts, lte, q0) : 0u;
+  m |= has_ut ? row_span_bits32(uts, ute, q0) : 0u;
+  return j >= N ? ~0u : m;
+}
+
+// Masks of a 64-key tile in the S^T layout (rows = keys in two 32-key blocks, columns = a wave's 32
+// query rows, one row per lane): lane c forms the masked-row word of key column c0 + c for the rows
+// q0 .. q0 + 31 and stores it in the wave's own 64-word LDS row; the wave then reads back the words of
+// the columns its registers hold. LDS operations of one wave run in order, and the wave-scope fences
+// keep the compiler from moving the read-back above the store.
+__device__ __forceinline__ void tile_column_words(uint32_t* cw, const i32x4* vec, int q0, int c0, int N, bool causal,
+                                                  bool has_lt, bool has_ut, int lane) {
+  const i32x4 mv = vec[lane];
+  cw[lane] = masked_row_bits32(q0, c0 + lane, N, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Words of the four key columns 32 jb + 8 q4 + 4 g + e (e = 0..3) held by accumulator registers
+// 4 q4 .. 4 q4 + 3 of block jb.
+__device__ __forceinline__ i32x4 column_words4(const uint32_t* cw, int jb, int q4, int g) {
+  return *reinterpret_cast<const i32x4*>(cw + jb * 32 + 8 * q4 + 4 * g);
+}
+
+// All ones when bit `row_bit` of the word is set (the lane's row is masked), else zero.
+__device__ __forceinline__ int row_mask_of(int word, int row_bit) { return (int)((uint32_t)word << (31 - row_bit)) >> 31; }
+
+// -inf where the given all-ones / all-zeros word is set, x elsewhere.
+__device__ __forceinline__ float select_neg_inf(int all_ones_if_masked, float x) {
+  const uint32_t m = (uint32_t)all_ones_if_masked;
+  return __uint_as_float((__float_as_uint(x) & ~m) | (0xff800000u & m));
 }
 
 // ------------------------------------------------------------------ matrix-core traits

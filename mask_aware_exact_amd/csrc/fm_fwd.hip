@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) T k_lds[2][BC * KLP];
   __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VLP];
   __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
+  __shared__ __attribute__((aligned(16))) uint32_t cw_lds[4][BC];  // per wave: masked-row words of a tile
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -217,17 +218,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
     float mx = -INFINITY;
     if (need_mask) {
+      tile_column_words(cw_lds[wave], vec_lds[buf], r0 + wave * 32, c0, N, causal, has_lt, has_ut, lane);
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
+          const i32x4 w4 = column_words4(cw_lds[wave], jb, q4, g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int jl = jb * 32 + 8 * q4 + 4 * g + e;
-            const int j = c0 + jl;
-            const i32x4 mv = vec_lds[buf][jl];
-            const bool msk = (j >= N) | masked_elem(row, j, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
-            const float x = msk ? -INFINITY : s[jb][4 * q4 + e];
+            const float x = select_neg_inf(row_mask_of(w4[e], l32), s[jb][4 * q4 + e]);
             s[jb][4 * q4 + e] = x;
             mx = fmaxf(mx, x);
           }
