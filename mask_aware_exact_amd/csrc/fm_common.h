@@ -375,15 +375,31 @@ __device__ __forceinline__ void copy_tile_async(bf16* tile, const bf16* __restri
   constexpr int NI = ROWS / RPI;   // instructions per tile
   constexpr int CPW = RB / 16;     // 16-byte chunks per row
   static_assert(ROWS % RPI == 0 && NI % NW == 0, "the tile must split evenly over the waves");
-  const int rl = lane / CPW, pos = lane % CPW;
+  // A wave's instructions step NW * RPI rows, a multiple of 16, so the swizzle key (a function of the
+  // row's low four bits) and hence the lane's source chunk stay the same for all of them.
+  static_assert((NW * RPI) % 16 == 0, "the swizzle key of a lane's row must not change between instructions");
+  const int rl = wave * RPI + lane / CPW;                            // lane's row for the first instruction
+  const int col = ((lane % CPW) ^ swz_key<D>(rl)) << 4;              // byte offset of its chunk in the row
+  const char* gb = reinterpret_cast<const char*>(g + (size_t)row0 * D);  // uniform
+  const int lim = nrows - 1 - row0;                                   // last valid row of the tile
+  typedef __attribute__((address_space(3))) void lds_void;
+  if (lim >= ROWS - 1) {
+    // whole tile in range: uniform base plus a constant 32-bit lane offset per instruction
+    const uint32_t off = (uint32_t)(rl * RB + col);
 #pragma unroll
-  for (int k = 0; k < NI / NW; ++k) {
-    const int i = __builtin_amdgcn_readfirstlane(wave + k * NW);
-    const int r = i * RPI + rl;
-    const int gr = min(row0 + r, nrows - 1);
-    const bf16* src = g + (size_t)gr * D + ((pos ^ swz_key<D>(r)) << 3);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(tile) + i * 1024),
-                                     16, 0, 0);
+    for (int k = 0; k < NI / NW; ++k) {
+      const int i = __builtin_amdgcn_readfirstlane(wave + k * NW);
+      __builtin_amdgcn_global_load_lds(gb + k * NW * RPI * RB + off, (lds_void*)(reinterpret_cast<char*>(tile) + i * 1024),
+                                       16, 0, 0);
+    }
+  } else {
+    // ragged last tile: rows past nrows read row nrows - 1 (finite data the kernels mask)
+#pragma unroll
+    for (int k = 0; k < NI / NW; ++k) {
+      const int i = __builtin_amdgcn_readfirstlane(wave + k * NW);
+      const uint32_t off = (uint32_t)(min(rl + k * NW * RPI, lim) * RB + col);
+      __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(reinterpret_cast<char*>(tile) + i * 1024), 16, 0, 0);
+    }
   }
 }
 
