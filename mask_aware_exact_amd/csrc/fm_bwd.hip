@@ -291,12 +291,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ 2a. dK / dV, bf16, wave pairs
 
-// Eight waves per 128-key tile: waves w and w + 4 share the 32 keys of group w % 4 and split the work so
-// that each stays under 256 registers (two waves per SIMD):
-//   role 0 (w < 4) holds K, forms S = Q K^T and P, and writes P to LDS;
-//   role 1 (w >= 4) holds V, forms dP = dO V^T, reads P back, forms dS and writes it to LDS;
-//   each role accumulates dV and dK for one half of the d columns.
-// While one wave of a SIMD runs its exponentials or dS arithmetic the other issues matrix products.
+// Eight waves per 128-key tile: waves w and w + 4 share the 32 keys of group w % 4 (one key column per
+// lane) and split the work so that each stays under 256 registers (two waves per SIMD):
+//   role 0 (w < 4) holds K, forms S = Q K^T and P, passes P to its partner through LDS and accumulates
+//     all of dV += P^T dO;
+//   role 1 (w >= 4) holds V, forms dP = dO V^T and dS = P o (dP - D) and accumulates all of dK += dS^T Q.
+// Two barriers per query tile t. Phase 1: role 0 forms S_t and P_t (exponentials) while role 1 issues
+// dP_t and the dK products of tile t - 1, whose dS it kept in registers. Phase 2: role 0 issues the dV
+// products of tile t while role 1 forms dS_t. So one wave of a SIMD runs vector arithmetic while the
+// other issues matrix products. Q is kept for three tiles (t - 1, t and the prefetched t + 1).
 template <int D>
 struct PairTraits {
   static constexpr int BC = 128;          // keys per workgroup
@@ -304,7 +307,6 @@ struct PairTraits {
   static constexpr int NT = 512;
   static constexpr int NKF = D / 16;      // K or V fragments per lane (k = d)
   static constexpr int NDB = D / 32;      // 32-wide d blocks
-  static constexpr int HDB = NDB / 2;     // d blocks per role
   static constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
   static constexpr int CH = BR * CPR / NT;
   static_assert(BR * CPR % NT == 0, "tile copies must divide evenly");
@@ -315,13 +317,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Tr = PairTraits<D>;
   using M = MM<bf16>;
   constexpr int BC = Tr::BC, BR = Tr::BR, CPR = Tr::CPR, CH = Tr::CH;
-  // Q and dO tiles are swizzled and unpadded (rows of D elements), two of each (double buffer).
-  __shared__ __attribute__((aligned(16))) bf16 q_lds[2 * BR * D];
-  __shared__ __attribute__((aligned(16))) bf16 do_lds[2 * BR * D];
-  // P and dS pass between the two waves of a key group in register order, lane-interleaved: chunk k
-  // (4 values) of lane l sits at [group][k][l], so every 8-byte access of a wave is 512 contiguous bytes.
+  constexpr int TILE = BR * D;
+  // Swizzled, unpadded Q (ring of three) and dO (two) tiles.
+  __shared__ __attribute__((aligned(16))) bf16 q_lds[3 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 do_lds[2 * TILE];
+  // P passes from role 0 to role 1 in register order, lane-interleaved: chunk k (4 values) of lane l sits
+  // at [group][k][l], so every 8-byte access of a wave is 512 contiguous bytes.
   __shared__ __attribute__((aligned(16))) bf16x4 p_xch[4][8][64];
-  __shared__ __attribute__((aligned(16))) bf16x4 s_xch[4][8][64];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BR];
   __shared__ __attribute__((aligned(16))) float dd_lds[2][BR];
 
@@ -375,17 +377,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     }
   }
   SwzRowReads<D> rrd;
-  SwzColReads<D, Tr::HDB> crd;
+  SwzColReads<D> crd;
   rrd.init(lane);
-  crd.init(lane, role * Tr::HDB);
+  crd.init(lane);
 
-  f32x16 dk[Tr::HDB], dv[Tr::HDB];
+  // dV^T (role 0) or dK^T (role 1) for this lane's key column, all of d.
+  f32x16 acc[Tr::NDB];
 #pragma unroll
-  for (int hb = 0; hb < Tr::HDB; ++hb) {
-    dk[hb] = zero16();
-    dv[hb] = zero16();
-  }
-  const int db0 = role * Tr::HDB;  // first d block of this role
+  for (int db = 0; db < Tr::NDB; ++db) acc[db] = zero16();
 
   const TileBounds bnd = merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N);
   const int nq = (N + BR - 1) / BR;
@@ -415,9 +414,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       ddr = ddg[i];
     }
   };
-  auto stash = [&](int buf) {
-    char* qb = reinterpret_cast<char*>(q_lds + buf * BR * D);
-    char* db_ = reinterpret_cast<char*>(do_lds + buf * BR * D);
+  auto stash = [&](int qs, int ds) {
+    char* qb = reinterpret_cast<char*>(q_lds + qs * TILE);
+    char* db_ = reinterpret_cast<char*>(do_lds + ds * TILE);
 #pragma unroll
     for (int it = 0; it < CH; ++it) {
       const int c = it * Tr::NT + tid;
@@ -428,111 +427,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     if (tid < BR) {
       // rows past N and rows without any unmasked key (lse = -inf) get +inf: exp(S - lse) = 0 for them
       const float l = (l_row >= N || lr == -INFINITY) ? INFINITY : lr;
-      lse_lds[buf][tid] = l * LOG2E;
-      dd_lds[buf][tid] = ddr;
+      lse_lds[ds][tid] = l * LOG2E;
+      dd_lds[ds][tid] = ddr;
     }
   };
 
-  TileWindow win = empty_window();
-  int qt = next_live_tile(win, qt_begin, nq, class_of, lane);
-  if (qt < nq) fetch(qt);
-  int buf = 0;
-
-  while (qt < nq) {
-    const int q0 = qt * BR;
-    const bool need_mask = window_partial(win, qt) || (q0 + BR > N) || (c0 + BC > N);
-    stash(buf);
-    __syncthreads();  // (A) the tile is in LDS; every wave is past the previous tile's reads
-    const int qt_next = next_live_tile(win, qt + 1, nq, class_of, lane);
-    if (qt_next < nq) fetch(qt_next);
-
-    const bf16* qb = q_lds + buf * BR * D;
-    const bf16* dob = do_lds + buf * BR * D;
-    const bf16* xb = role == 0 ? qb : dob;
-
-    // Phase 1: role 0 forms S and P, role 1 forms dP (rows = query rows, columns = this lane's keys).
-    __builtin_amdgcn_s_setprio(2);
-    f32x16 x[2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      x[ib] = zero16();
-#pragma unroll
-      for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(xb, ib, c), xf[c], x[ib]);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    bf16x4 pv[2][4];  // P (role 0: computed, role 1: read back), register order
-    if (role == 0) {
-      if (need_mask) {
-        const uint64_t mbits = masked_row_bits(q0, j, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
-        const uint32_t mlo = (uint32_t)(mbits >> (4 * g)), mhi = (uint32_t)(mbits >> (32 + 4 * g));
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const uint32_t mw = ib == 0 ? mlo : mhi;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int il0 = ib * 32 + 8 * q4 + 4 * g;
-            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p = __builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
-              pv[ib][q4][e] = (bf16)(((mw >> (8 * q4 + e)) & 1u) ? 0.f : p);
-            }
-            p_xch[kgrp][4 * ib + q4][lane] = pv[ib][q4];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int il0 = ib * 32 + 8 * q4 + 4 * g;
-            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][il0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pv[ib][q4][e] = (bf16)__builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
-            p_xch[kgrp][4 * ib + q4][lane] = pv[ib][q4];
-          }
-        }
-      }
-    }
-    __syncthreads();  // (B) P is in LDS
-
-    // Phase 2: role 1 reads P, forms dS and writes it; both roles accumulate their half of dV.
-    bf16x4 sv[2][4];  // dS, register order
-    if (role == 1) {
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int il0 = ib * 32 + 8 * q4 + 4 * g;
-          pv[ib][q4] = p_xch[kgrp][4 * ib + q4][lane];
-          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[buf][il0]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)pv[ib][q4][e] * (x[ib][4 * q4 + e] - dd4[e]));
-          s_xch[kgrp][4 * ib + q4][lane] = sv[ib][q4];
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = pv[t >> 1][2 * (t & 1)][e];
-        pf[4 + e] = pv[t >> 1][2 * (t & 1) + 1][e];
-      }
-#pragma unroll
-      for (int hb = 0; hb < Tr::HDB; ++hb) dv[hb] = M::mma(crd.read(dob, t, hb), pf, dv[hb]);
-    }
-    __syncthreads();  // (C) dS is in LDS
-
-    // Phase 3: role 0 reads dS back; both roles accumulate their half of dK.
-    if (role == 0) {
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) sv[ib][q4] = s_xch[kgrp][4 * ib + q4][lane];
-      }
-    }
+  // dK^T += Q^T dS for one query tile, dS in register order (role 1).
+  auto dk_products = [&](const bf16x4 (&sv)[2][4], const bf16* qb) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bf16x8 sf;
@@ -542,29 +443,128 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         sf[4 + e] = sv[t >> 1][2 * (t & 1) + 1][e];
       }
 #pragma unroll
-      for (int hb = 0; hb < Tr::HDB; ++hb) dk[hb] = M::mma(crd.read(qb, t, hb), sf, dk[hb]);
+      for (int db = 0; db < Tr::NDB; ++db) acc[db] = M::mma(crd.read(qb, t, db), sf, acc[db]);
     }
-    qt = qt_next;
-    buf ^= 1;
-  }
+  };
 
-  // dK = scale * dK^T, dV = dV^T for this lane's key column and this role's half of d.
-  if (j < N) {
-    bf16* dkg = static_cast<bf16*>(a.dk) + head + (size_t)j * D;
-    bf16* dvg = static_cast<bf16*>(a.dv) + head + (size_t)j * D;
+  TileWindow win = empty_window();
+  int qt = next_live_tile(win, qt_begin, nq, class_of, lane);
+  if (qt < nq) fetch(qt);
+  int qs = 0, ds = 0;     // ring slots of the current tile's Q and dO (and lse / D)
+  int qs_prev = -1;       // role 1: slot of the previous tile's Q, whose dS is still pending
+  bf16x4 sv[2][4];        // role 1: that dS, register order
+
+  while (qt < nq) {
+    const int q0 = qt * BR;
+    const bool need_mask = window_partial(win, qt) || (q0 + BR > N) || (c0 + BC > N);
+    stash(qs, ds);
+    __syncthreads();  // (A) the tile is in LDS; every wave is past the previous tile's work
+    const int qt_next = next_live_tile(win, qt + 1, nq, class_of, lane);
+    if (qt_next < nq) fetch(qt_next);
+
+    const bf16* qb = q_lds + qs * TILE;
+    const bf16* dob = do_lds + ds * TILE;
+
+    // Phase 1. Role 0: S (rows = query rows, columns = this lane's keys) and P, written to LDS.
+    // Role 1: dP, then the dK products of the previous tile.
+    bf16x4 pv[2][4];  // P, register order
+    f32x16 x[2];
+    if (role == 0) {
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-    for (int hb = 0; hb < Tr::HDB; ++hb) {
+      for (int ib = 0; ib < 2; ++ib) {
+        x[ib] = zero16();
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = (db0 + hb) * 32 + 8 * q4 + 4 * g;
-        bf16x4 wk, wv;
+        for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(qb, ib, c), xf[c], x[ib]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (need_mask) {
+        const uint64_t mbits = masked_row_bits(q0, j, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
+        const uint32_t mlo = (uint32_t)(mbits >> (4 * g)), mhi = (uint32_t)(mbits >> (32 + 4 * g));
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const uint32_t mw = ib == 0 ? mlo : mhi;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float xm = select_neg_inf(row_mask_of((int)mw, 8 * q4 + e), x[ib][4 * q4 + e]);
+              pv[ib][q4][e] = (bf16)__builtin_amdgcn_exp2f(xm * sl2 - lse4[e]);
+            }
+            p_xch[kgrp][4 * ib + q4][lane] = pv[ib][q4];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[ib][q4][e] = (bf16)__builtin_amdgcn_exp2f(x[ib][4 * q4 + e] * sl2 - lse4[e]);
+            p_xch[kgrp][4 * ib + q4][lane] = pv[ib][q4];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        x[ib] = zero16();
+#pragma unroll
+        for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
+      }
+      if (qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
+    }
+    __syncthreads();  // (B) P is in LDS
+
+    // Phase 2. Role 0: dV^T += dO^T P. Role 1: reads P back and forms dS, kept for the next tile.
+    if (role == 0) {
+      __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          wk[e] = (bf16)(dk[hb][4 * q4 + e] * a.scale);
-          wv[e] = (bf16)dv[hb][4 * q4 + e];
+          pf[e] = pv[t >> 1][2 * (t & 1)][e];
+          pf[4 + e] = pv[t >> 1][2 * (t & 1) + 1][e];
         }
-        *reinterpret_cast<bf16x4*>(dkg + d0) = wk;
-        *reinterpret_cast<bf16x4*>(dvg + d0) = wv;
+#pragma unroll
+        for (int db = 0; db < Tr::NDB; ++db) acc[db] = M::mma(crd.read(dob, t, db), pf, acc[db]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const bf16x4 p4 = p_xch[kgrp][4 * ib + q4][lane];
+          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)p4[e] * (x[ib][4 * q4 + e] - dd4[e]));
+        }
+      }
+      qs_prev = qs;
+    }
+    qt = qt_next;
+    qs = qs == 2 ? 0 : qs + 1;
+    ds ^= 1;
+  }
+  // Role 1: the dK products of the last tile (its Q is still in LDS: nothing has been stored since).
+  if (role == 1 && qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
+
+  // dV = dV^T (role 0) or dK = scale * dK^T (role 1) for this lane's key column, all of d.
+  if (j < N) {
+    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + head + (size_t)j * D;
+    const float mul = role == 0 ? 1.f : a.scale;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * q4 + e] * mul);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * q4 + 4 * g) = w;
       }
     }
   }
