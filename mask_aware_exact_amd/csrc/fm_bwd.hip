@@ -508,13 +508,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         }
       }
     } else {
+      if (qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         x[ib] = zero16();
 #pragma unroll
         for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
       }
-      if (qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
     }
     __syncthreads();  // (B) P is in LDS
 
