@@ -362,6 +362,21 @@ struct SwzColReads {  // operand with k along the rows (the load_kmajor_frag pat
   }
 };
 
+// One direct global-to-LDS copy instruction: each lane fetches 16 bytes from gbase + voff and the wave
+// writes them lane-linearly at LDS byte address lds (wave-uniform). Issued as inline assembly: the
+// compiler's wait-count pass models the builtin as a store to an unknown LDS location and would then
+// wait for every copy in flight before any later LDS read, which serialises each prefetch with the
+// compute it should overlap. Callers wait themselves (s_waitcnt vmcnt(0) and a barrier) before reading
+// the tile; the compiler only ever over-waits for its own loads because of these untracked ones.
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
+}
+
+// LDS byte address of a pointer into shared memory, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
 // Asynchronous copy of rows [row0, row0 + ROWS) of a [*, D] bf16 matrix into a swizzled LDS tile with
 // direct global-to-LDS loads: each wave instruction moves 1 KB (16 bytes per lane, written lane-linearly
 // at the instruction's LDS address), and lane l of the instruction fetches the global chunk that the
@@ -382,23 +397,18 @@ __device__ __forceinline__ void copy_tile_async(bf16* tile, const bf16* __restri
   const int col = ((lane % CPW) ^ swz_key<D>(rl)) << 4;              // byte offset of its chunk in the row
   const char* gb = reinterpret_cast<const char*>(g + (size_t)row0 * D);  // uniform
   const int lim = nrows - 1 - row0;                                   // last valid row of the tile
-  typedef __attribute__((address_space(3))) void lds_void;
+  const uint32_t lds0 = lds_addr(tile) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
   if (lim >= ROWS - 1) {
     // whole tile in range: uniform base plus a constant 32-bit lane offset per instruction
     const uint32_t off = (uint32_t)(rl * RB + col);
 #pragma unroll
-    for (int k = 0; k < NI / NW; ++k) {
-      const int i = __builtin_amdgcn_readfirstlane(wave + k * NW);
-      __builtin_amdgcn_global_load_lds(gb + k * NW * RPI * RB + off, (lds_void*)(reinterpret_cast<char*>(tile) + i * 1024),
-                                       16, 0, 0);
-    }
+    for (int k = 0; k < NI / NW; ++k) lds_copy16(gb + k * NW * RPI * RB, off, lds0 + k * NW * 1024);
   } else {
     // ragged last tile: rows past nrows read row nrows - 1 (finite data the kernels mask)
 #pragma unroll
     for (int k = 0; k < NI / NW; ++k) {
-      const int i = __builtin_amdgcn_readfirstlane(wave + k * NW);
       const uint32_t off = (uint32_t)(min(rl + k * NW * RPI, lim) * RB + col);
-      __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(reinterpret_cast<char*>(tile) + i * 1024), 16, 0, 0);
+      lds_copy16(gb, off, lds0 + k * NW * 1024);
     }
   }
 }
