@@ -307,18 +307,15 @@ struct PairTraits {
   static constexpr int NT = 512;
   static constexpr int NKF = D / 16;      // K or V fragments per lane (k = d)
   static constexpr int NDB = D / 32;      // 32-wide d blocks
-  static constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
-  static constexpr int CH = BR * CPR / NT;
-  static_assert(BR * CPR % NT == 0, "tile copies must divide evenly");
 };
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Tr = PairTraits<D>;
   using M = MM<bf16>;
-  constexpr int BC = Tr::BC, BR = Tr::BR, CPR = Tr::CPR, CH = Tr::CH;
+  constexpr int BC = Tr::BC, BR = Tr::BR;
   constexpr int TILE = BR * D;
-  // Swizzled, unpadded Q (ring of three) and dO (two) tiles.
+  // Swizzled, unpadded Q (ring of three) and dO (two) tiles, filled by direct global-to-LDS copies.
   __shared__ __attribute__((aligned(16))) bf16 q_lds[3 * TILE];
   __shared__ __attribute__((aligned(16))) bf16 do_lds[2 * TILE];
   // P passes from role 0 to role 1 in register order, lane-interleaved: chunk k (4 values) of lane l sits
@@ -391,39 +388,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   const int qt_begin = causal ? c0 / BR : 0;
   auto class_of = [&](int qt) { return classify_tile(qt * BR, min(N, qt * BR + BR), c0, c1, bnd, causal); };
 
-  // Prefetch registers for one query tile. Loads are unconditional (rows past N read row N - 1, whose
-  // values are finite; those rows get lse = +inf and are masked, so they contribute nothing) so that
-  // nothing waits on them before the next iteration stores them.
-  i32x4 qr[CH], dr[CH];
+  // Next query tile: Q and dO straight into their ring slots (direct global-to-LDS copies; rows past N
+  // read row N - 1, which gets lse = +inf below and so contributes nothing), lse and D into registers.
   float lr = 0.f, ddr = 0.f;
   int l_row = 0;
-  auto fetch = [&](int qt) {
+  auto fetch = [&](int qt, int qslot, int dslot) {
     const int q0 = qt * BR;
-#pragma unroll
-    for (int it = 0; it < CH; ++it) {
-      const int c = it * Tr::NT + tid;
-      const int r = c / CPR, cc = c % CPR;
-      const size_t rr = (size_t)min(q0 + r, N - 1);
-      qr[it] = ld16(reinterpret_cast<const char*>(qg + rr * D) + cc * 16);
-      dr[it] = ld16(reinterpret_cast<const char*>(dog + rr * D) + cc * 16);
-    }
     if (tid < BR) {
       l_row = q0 + tid;
       const int i = min(l_row, N - 1);
       lr = lseg[i];
       ddr = ddg[i];
     }
+    copy_tile_async<D, BR, 8>(q_lds + qslot * TILE, qg, q0, N, wave, lane);
+    copy_tile_async<D, BR, 8>(do_lds + dslot * TILE, dog, q0, N, wave, lane);
   };
-  auto stash = [&](int qs, int ds) {
-    char* qb = reinterpret_cast<char*>(q_lds + qs * TILE);
-    char* db_ = reinterpret_cast<char*>(do_lds + ds * TILE);
-#pragma unroll
-    for (int it = 0; it < CH; ++it) {
-      const int c = it * Tr::NT + tid;
-      const int r = c / CPR, cc = c % CPR;
-      st16(qb + swz_off<D>(r, cc * 8), qr[it]);
-      st16(db_ + swz_off<D>(r, cc * 8), dr[it]);
-    }
+  auto stash = [&](int ds) {
     if (tid < BR) {
       // rows past N and rows without any unmasked key (lse = -inf) get +inf: exp(S - lse) = 0 for them
       const float l = (l_row >= N || lr == -INFINITY) ? INFINITY : lr;
@@ -449,7 +429,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
   TileWindow win = empty_window();
   int qt = next_live_tile(win, qt_begin, nq, class_of, lane);
-  if (qt < nq) fetch(qt);
+  if (qt < nq) fetch(qt, 0, 0);
   int qs = 0, ds = 0;     // ring slots of the current tile's Q and dO (and lse / D)
   int qs_prev = -1;       // role 1: slot of the previous tile's Q, whose dS is still pending
   bf16x4 sv[2][4];        // role 1: that dS, register order
@@ -457,10 +437,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   while (qt < nq) {
     const int q0 = qt * BR;
     const bool need_mask = window_partial(win, qt) || (q0 + BR > N) || (c0 + BC > N);
-    stash(qs, ds);
+    stash(ds);
+    __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();  // (A) the tile is in LDS; every wave is past the previous tile's work
     const int qt_next = next_live_tile(win, qt + 1, nq, class_of, lane);
-    if (qt_next < nq) fetch(qt_next);
+    if (qt_next < nq) fetch(qt_next, qs == 2 ? 0 : qs + 1, ds ^ 1);
 
     const bf16* qb = q_lds + qs * TILE;
     const bf16* dob = do_lds + ds * TILE;
