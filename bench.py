@@ -176,6 +176,44 @@ def time_workload(fm, wl: Workload, steps: int, warmup: int):
     return wall, parts.mean(axis=0), ok
 
 
+def time_workload_compacted(fm, wl: Workload, steps: int, warmup: int):
+    """The same step through key compaction: fm_compact_keys, fm_gather_rows (K, V), fm_tile_bounds,
+    fm_fwd and fm_bwd without the causal flag, fm_gather_rows (dK, dV back). All of it is timed."""
+    import torch
+    dev = wl.q.device
+    Hm = wl.spec.Hm
+    dk, dv = torch.empty_like(wl.k), torch.empty_like(wl.v)
+    ws = torch.empty(fm.fm_bwd_workspace_bytes(torch.bfloat16, wl.B, wl.H, wl.N, wl.d), dtype=torch.uint8,
+                     device=dev)
+    bounds = torch.empty(fm.fm_bounds_elems(wl.B, Hm, wl.N), dtype=torch.int32, device=dev)
+    k2, v2 = torch.empty_like(wl.k), torch.empty_like(wl.v)
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    dq, dk2, dv2 = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
+
+    def step():
+        kidx, kpos, counts, vecs2 = fm.fm_compact_keys(*wl.vecs, wl.B, Hm, wl.N, wl.spec.causal)
+        fm.fm_gather_rows(wl.k, kidx, y=k2)
+        fm.fm_gather_rows(wl.v, kidx, y=v2)
+        b = fm.fm_tile_bounds(*vecs2, wl.B, Hm, wl.N, bounds=bounds)
+        fm.fm_fwd(wl.q, k2, v2, *vecs2, bounds=b, causal=False, scale=wl.scale, out=out, lse=lse)
+        fm.fm_bwd(wl.q, k2, v2, out, wl.do, lse, *vecs2, bounds=b, causal=False, scale=wl.scale, dq=dq, dk=dk2,
+                  dv=dv2, workspace=ws)
+        fm.fm_gather_rows(dk2, kpos, y=dk)
+        fm.fm_gather_rows(dv2, kpos, y=dv)
+        return counts
+
+    for _ in range(warmup):
+        counts = step()
+    torch.cuda.synchronize()
+    ok = int(counts.min()) >= 0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, ok
+
+
 def cpu_baseline(wl: Workload, budget_heads: int, max_tokens: int):
     """The oracle, as it stands, timed on a bounded sample of the same workload: the first heads and
     the first `max_tokens` tokens (for a causal mask the leading tokens form a closed sub-problem)."""
@@ -285,6 +323,14 @@ def main():
             sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
                            "U": int(wl.U), "fwd_ms": round(float(p2[1]), 3), "bwd_ms": round(float(p2[2]), 3),
                            "bounds_ms": round(float(p2[0]), 4), "finite": ok2}
+        del wl
+        torch.cuda.empty_cache()
+        wl = Workload("dpo_rm_causal_key_drop", dev)
+        n = max(3, args.steps // 4)
+        w3, ok3 = time_workload_compacted(fm, wl, n, 1)
+        sweep["dpo_rm_causal_key_drop (key compaction)"] = {
+            "TFLOP/s": round(wl.flop / (w3 * 1e3 / n * 1e-3) / 1e12, 2), "ms_per_step": round(w3 * 1e3 / n, 3),
+            "U": int(wl.U), "compactable": ok3}
         rec["sweep"] = sweep
     print(json.dumps(rec), flush=True)
 

@@ -107,6 +107,35 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
                  const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Key compaction for masks that drop whole key columns (per-head key dropping with compute reduced in
+ * proportion to the keys kept: SCFA review, nubint.ai, "proposed method"). A column is dropped when it
+ * is masked for every query row i in [0, N) (its causal rows, LT and UT together cover [0, N)). For each
+ * (b, hm) row of the mask vectors [B, Hm, N]:
+ *   counts[b, hm]      number of kept columns K, or -1 if some kept column needs three disjoint row
+ *                      intervals (causal rows [0, j) plus two disjoint, non-adjacent spans), which the
+ *                      compacted mask cannot hold; the other outputs of that row are then unspecified;
+ *   kidx[b, hm, r]     original index of the r-th kept column (increasing), -1 for r >= K;
+ *   kpos[b, hm, j]     position of column j among the kept ones, -1 if dropped;
+ *   lts2 .. ute2       the mask of the compacted problem, to be run with causal = 0: kept position r
+ *                      holds column j's spans clipped to [0, N], with the causal rows [0, j) merged into
+ *                      the UT span (or, if UT starts after j, into the LT span); positions r >= K mask
+ *                      every row (LT = [0, N), UT empty). Empty spans are canonical (LT N, N; UT 0, 0).
+ * Running fm_fwd / fm_bwd on K, V gathered by kidx (fm_gather_rows) with these vectors gives the same
+ * out, lse and dq as the original problem; dk, dv come back by gathering with kpos. All outputs are
+ * int32 device arrays owned by the caller; a NULL pair of inputs is an empty span.
+ * Errors: FM_ERR_INVALID (NULL outputs, sizes out of range, half-NULL pair), FM_ERR_LAUNCH. */
+fm_status fm_compact_keys(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int B,
+                          int Hm, int N, int causal, int32_t* kidx, int32_t* kpos, int32_t* counts, int32_t* lts2,
+                          int32_t* lte2, int32_t* uts2, int32_t* ute2, hipStream_t stream);
+
+/* Row gather: y[b, h, r, :] = x[b, h, idx[b, hm, r], :] with hm = (Hm == H ? h : 0), and zero where
+ * idx is negative. x, y are contiguous [B, H, N, d] of dtype (16-byte aligned), idx is int32
+ * [B, Hm, N] with values in [-1, N) (others give a zero row). With kidx it builds the compacted K and
+ * V; with kpos it scatters the compacted dK and dV back to the original order. y must not alias x.
+ * Errors: FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_LAUNCH. */
+fm_status fm_gather_rows(const void* x, fm_dtype dtype, int B, int H, int N, int d, const int32_t* idx, int Hm,
+                         void* y, hipStream_t stream);
+
 /* Test hook: the tile classifier the kernels use, materialised. For each (b, hm, query tile of
  * qblock rows, key tile of kblock columns), clipped to N, writes classes[b][hm][qt][kt]:
  *   2 FULL    the causal triangle or one interval covers every (row, column) of the tile

@@ -2,7 +2,8 @@
 
 Argument marshalling only: torch supplies device memory and the current stream, every step of the
 path runs in the HIP kernels behind the C ABI declared in include/fm.h. The entry points keep the C
-names: fm_tile_bounds, fm_fwd, fm_bwd (plus fm_tile_classes, a test hook). There is no fallback:
+names: fm_tile_bounds, fm_fwd, fm_bwd, the key-compaction pair fm_compact_keys and fm_gather_rows
+(plus fm_tile_classes, a test hook). There is no fallback:
 if libfm.so is missing or cannot be loaded, every call raises.
 """
 from __future__ import annotations
@@ -20,7 +21,8 @@ FM_BF16, FM_F32 = 0, 1
 NONE, PARTIAL, FULL = 0, 1, 2
 
 EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_fwd",
-            "fm_bwd_workspace_bytes", "fm_bwd", "fm_tile_classes", "fm_status_str")
+            "fm_bwd_workspace_bytes", "fm_bwd", "fm_tile_classes", "fm_compact_keys", "fm_gather_rows",
+            "fm_status_str")
 
 
 class FmError(RuntimeError):
@@ -57,6 +59,10 @@ def load_library(path: str = LIB_PATH):
     lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P, P, S, P]
     lib.fm_tile_classes.restype = I
     lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
+    lib.fm_compact_keys.restype = I
+    lib.fm_compact_keys.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P]
+    lib.fm_gather_rows.restype = I
+    lib.fm_gather_rows.argtypes = [P, I, I, I, I, I, P, I, P, P]
     lib.fm_status_str.restype = ctypes.c_char_p
     lib.fm_status_str.argtypes = [I]
     _lib = lib
@@ -189,3 +195,32 @@ def fm_tile_classes(bounds, B: int, Hm: int, N: int, causal: bool, qblock: int, 
     _check(lib.fm_tile_classes(_ptr(bounds), B, Hm, N, int(bool(causal)), qblock, _ptr(classes),
                                _stream(stream)), "fm_tile_classes")
     return classes.view(B, Hm, nq, nk)
+
+
+def fm_compact_keys(lts, lte, uts, ute, B: int, Hm: int, N: int, causal: bool, stream=None):
+    """Kept-column compaction of the mask (see include/fm.h). Returns (kidx, kpos, counts, vectors) with
+    kidx, kpos int32 [B, Hm, N], counts int32 [B, Hm] and vectors the four int32 [B, Hm, N] arrays of
+    the compacted problem (to be run with causal = False). Asynchronous: counts of -1 (a column the
+    compacted mask cannot hold) are the caller's to check."""
+    lib = load_library()
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    _need_cuda(*vecs)
+    dev = next((x.device for x in vecs if x is not None), torch.device("cuda"))
+    new = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)  # noqa: E731
+    kidx, kpos, counts = new(B, Hm, N), new(B, Hm, N), new(B, Hm)
+    out = [new(B, Hm, N) for _ in range(4)]
+    _check(lib.fm_compact_keys(*[_ptr(x) for x in vecs], B, Hm, N, int(bool(causal)), _ptr(kidx), _ptr(kpos),
+                               _ptr(counts), *[_ptr(x) for x in out], _stream(stream)), "fm_compact_keys")
+    return kidx, kpos, counts, out
+
+
+def fm_gather_rows(x, idx, y=None, stream=None):
+    """y[b, h, r] = x[b, h, idx[b, hm, r]] (zero where idx < 0) for x of shape [B, H, N, d]."""
+    lib = load_library()
+    B, H, N, d = x.shape
+    idx = _vec(idx)
+    _need_cuda(x, idx)
+    y = torch.empty_like(x) if y is None else y
+    _check(lib.fm_gather_rows(_ptr(x), _dtype_code(x), B, H, N, d, _ptr(idx), idx.shape[1], _ptr(y),
+                              _stream(stream)), "fm_gather_rows")
+    return y

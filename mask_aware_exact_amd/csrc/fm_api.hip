@@ -20,6 +20,11 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
                       const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int N, int Hm,
                       int causal, float scale, hipStream_t stream);
 int fwd_qblock();
+hipError_t launch_compact_keys(const int* lts, const int* lte, const int* uts, const int* ute, int rows, int N,
+                               int causal, int* kidx, int* kpos, int* counts, int* lts2, int* lte2, int* uts2,
+                               int* ute2, hipStream_t stream);
+hipError_t launch_gather_rows(const void* x, const int* idx, int B, int H, int Hm, int N, int row_bytes, void* y,
+                              hipStream_t stream);
 }  // namespace fm
 
 namespace {
@@ -114,6 +119,28 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
   float* dd = static_cast<float*>(workspace);
   return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dd, lts, lte, uts, ute,
                                  bounds, B, H, N, Hm, causal != 0, scale, stream));
+}
+
+fm_status fm_compact_keys(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int B,
+                          int Hm, int N, int causal, int32_t* kidx, int32_t* kpos, int32_t* counts, int32_t* lts2,
+                          int32_t* lte2, int32_t* uts2, int32_t* ute2, hipStream_t stream) {
+  if (kidx == nullptr || kpos == nullptr || counts == nullptr || lts2 == nullptr || lte2 == nullptr ||
+      uts2 == nullptr || ute2 == nullptr)
+    return FM_ERR_INVALID;
+  if (!sizes_ok(B, Hm, N) || !pair_ok(lts, lte) || !pair_ok(uts, ute)) return FM_ERR_INVALID;
+  return from_hip(fm::launch_compact_keys(lts, lte, uts, ute, B * Hm, N, causal != 0, kidx, kpos, counts, lts2,
+                                          lte2, uts2, ute2, stream));
+}
+
+fm_status fm_gather_rows(const void* x, fm_dtype dtype, int B, int H, int N, int d, const int32_t* idx, int Hm,
+                         void* y, hipStream_t stream) {
+  if (x == nullptr || idx == nullptr || y == nullptr || x == y) return FM_ERR_INVALID;
+  const fm_status st = dtype_d_ok(dtype, d);
+  if (st != FM_OK) return st;
+  if (!sizes_ok(B, H, N) || (Hm != 1 && Hm != H)) return FM_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return FM_ERR_INVALID;
+  const int row_bytes = d * (dtype == FM_BF16 ? 2 : 4);
+  return from_hip(fm::launch_gather_rows(x, idx, B, H, Hm, N, row_bytes, y, stream));
 }
 
 fm_status fm_tile_classes(const int32_t* bounds, int B, int Hm, int N, int causal, int qblock, uint8_t* classes,

@@ -13,5 +13,6 @@ Modules:
   masks     dense mask expansion, hand-written dense twins of each mask family, unmasked-pair count
   tiles     per-key-tile min/max of the four vectors and the FULL/PARTIAL/NONE tile rule
   attention fp64 forward/backward (row-blocked), brute force for tiny cases, one-row/one-column probes
+  compact   removal of the key columns masked for every row, and the compacted problem's mask
 """
-from . import masks, tiles, attention  # noqa: F401
+from . import masks, tiles, attention, compact  # noqa: F401

@@ -112,3 +112,22 @@ def compare(gpu: dict, ref: dict, dtype: str, report: dict | None = None):
 
 def oracle_bounds(spec: W.MaskSpec):
     return OT.tile_bounds(spec.vectors(), spec.B, spec.Hm, spec.N)
+
+
+def run_gpu_compacted(case: Case, fm, dev="cuda"):
+    """The same results through key compaction: fm_compact_keys -> fm_gather_rows (K, V) ->
+    fm_tile_bounds -> fm_fwd / fm_bwd without the causal flag -> fm_gather_rows (dK, dV back)."""
+    q, k, v, do = (t.to(dev) for t in (case.q, case.k, case.v, case.do))
+    vecs = device_vectors(case.spec, dev)
+    Hm = case.spec.Hm
+    kidx, kpos, counts, vecs2 = fm.fm_compact_keys(*vecs, case.B, Hm, case.N, case.spec.causal)
+    k2, v2 = fm.fm_gather_rows(k, kidx), fm.fm_gather_rows(v, kidx)
+    bounds = fm.fm_tile_bounds(*vecs2, case.B, Hm, case.N)
+    out, lse = fm.fm_fwd(q, k2, v2, *vecs2, bounds=bounds, causal=False, scale=case.scale)
+    dq, dk2, dv2 = fm.fm_bwd(q, k2, v2, out, do, lse, *vecs2, bounds=bounds, causal=False, scale=case.scale)
+    dk, dv = fm.fm_gather_rows(dk2, kpos), fm.fm_gather_rows(dv2, kpos)
+    torch.cuda.synchronize()
+    assert int(counts.min()) >= 0, "mask not compactable"
+    res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "kidx": kidx, "kpos": kpos, "counts": counts,
+           "vecs2": vecs2}
+    return {k_: ([x.cpu() for x in t] if isinstance(t, list) else t.cpu()) for k_, t in res.items()}

@@ -123,3 +123,40 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fm.fm_fwd(q, q, q)
+
+
+def _compact(lib, **kw):
+    args = dict(lts=A, lte=A, uts=None, ute=None, B=1, Hm=2, N=100, causal=1, kidx=A, kpos=A, counts=A,
+                lts2=A, lte2=A, uts2=A, ute2=A)
+    args.update(kw)
+    return lib.fm_compact_keys(args["lts"], args["lte"], args["uts"], args["ute"], args["B"], args["Hm"],
+                               args["N"], args["causal"], args["kidx"], args["kpos"], args["counts"],
+                               args["lts2"], args["lte2"], args["uts2"], args["ute2"], None)
+
+
+def test_compact_validation(lib):
+    for name in ("kidx", "kpos", "counts", "lts2", "lte2", "uts2", "ute2"):
+        assert _compact(lib, **{name: None}) == fm.FM_ERR_INVALID, name
+    assert _compact(lib, lte=None) == fm.FM_ERR_INVALID          # half-NULL pair
+    assert _compact(lib, uts=A) == fm.FM_ERR_INVALID
+    assert _compact(lib, B=0) == fm.FM_ERR_INVALID
+    assert _compact(lib, N=(1 << 24) + 1) == fm.FM_ERR_INVALID
+
+
+def _gather(lib, **kw):
+    args = dict(x=A, dtype=fm.FM_BF16, B=1, H=2, N=100, d=64, idx=A, Hm=1, y=P(0x200000))
+    args.update(kw)
+    return lib.fm_gather_rows(args["x"], args["dtype"], args["B"], args["H"], args["N"], args["d"], args["idx"],
+                              args["Hm"], args["y"], None)
+
+
+def test_gather_validation(lib):
+    assert _gather(lib, x=None) == fm.FM_ERR_INVALID
+    assert _gather(lib, idx=None) == fm.FM_ERR_INVALID
+    assert _gather(lib, y=None) == fm.FM_ERR_INVALID
+    assert _gather(lib, y=A) == fm.FM_ERR_INVALID                 # aliases x
+    assert _gather(lib, Hm=3) == fm.FM_ERR_INVALID
+    assert _gather(lib, d=96) == fm.FM_ERR_UNSUPPORTED
+    assert _gather(lib, dtype=5) == fm.FM_ERR_UNSUPPORTED
+    assert _gather(lib, y=P(0x200004)) == fm.FM_ERR_INVALID       # misaligned
+    assert _gather(lib, H=0) == fm.FM_ERR_INVALID

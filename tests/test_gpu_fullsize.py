@@ -110,3 +110,53 @@ def test_fullsize_sampled_parity(fm, name):
         print(f"  head ({bb},{hh}): rows {rows.size} cols {cols.size} ok", flush=True)
     del wl
     torch.cuda.empty_cache()
+
+
+def test_fullsize_key_drop_compacted(fm):
+    """The key-drop workload at full size through key compaction (fm_compact_keys, fm_gather_rows, the
+    attention without the causal flag, fm_gather_rows back): sampled rows and columns against the
+    oracle on the original problem, and the gradient invariants."""
+    name = "dpo_rm_causal_key_drop"
+    print(f"\nworkload {name} (compacted)", flush=True)
+    dev = torch.device("cuda:0")
+    wl = bench.Workload(name, dev)
+    Hm = wl.spec.Hm
+    kidx, kpos, counts, vecs2 = fm.fm_compact_keys(*wl.vecs, wl.B, Hm, wl.N, wl.spec.causal)
+    k2, v2 = fm.fm_gather_rows(wl.k, kidx), fm.fm_gather_rows(wl.v, kidx)
+    b2 = fm.fm_tile_bounds(*vecs2, wl.B, Hm, wl.N)
+    out, lse = fm.fm_fwd(wl.q, k2, v2, *vecs2, bounds=b2, causal=False, scale=wl.scale)
+    dq, dk2, dv2 = fm.fm_bwd(wl.q, k2, v2, out, wl.do, lse, *vecs2, bounds=b2, causal=False, scale=wl.scale)
+    dk, dv = fm.fm_gather_rows(dk2, kpos), fm.fm_gather_rows(dv2, kpos)
+    torch.cuda.synchronize()
+    assert int(counts.min()) >= 0
+    del k2, v2, dk2, dv2
+    rng = np.random.default_rng(5)
+    N, tol = wl.N, C.TOL["bf16"]
+    q_h, k_h, v_h, do_h = wl.host
+    for (bb, hh) in sorted({(0, 0), (wl.B - 1, wl.H - 1)}):
+        vecs = wl.spec.column_slice(bb, hh)
+        f64 = lambda x: torch.from_numpy(np.ascontiguousarray(x[bb, hh])).to(torch.bfloat16).to(  # noqa: E731
+            torch.float64).numpy()
+        q, k, v, do = f64(q_h), f64(k_h), f64(v_h), f64(do_h)
+        rows = _pick_rows(wl.spec, bb, hh, N, rng)
+        r_out, r_lse, _, r_dq = OA.rows_probe(q, k, v, do, vecs, wl.spec.causal, wl.scale, rows)
+        assert np.max(np.abs(out[bb, hh, rows].double().cpu().numpy() - r_out)) <= tol["out"]
+        g_lse = lse[bb, hh, rows].double().cpu().numpy()
+        fin = np.isfinite(r_lse)
+        assert np.array_equal(fin, np.isfinite(g_lse))
+        assert np.max(np.abs(g_lse[fin] - r_lse[fin]), initial=0.0) <= tol["lse"]
+        assert C.rel_fro(dq[bb, hh, rows].double().cpu().numpy(), r_dq) <= tol["grad"]
+        cols = _pick_cols(vecs, wl.spec.causal, N, rng)
+        if cols.size:
+            r_dk, r_dv = OA.cols_probe(q, k, v, do, vecs, wl.spec.causal, wl.scale, cols)
+            assert C.rel_fro(dk[bb, hh, cols].double().cpu().numpy(), r_dk) <= tol["grad"]
+            assert C.rel_fro(dv[bb, hh, cols].double().cpu().numpy(), r_dv) <= tol["grad"]
+        dropped = kpos[bb, hh if Hm > 1 else 0].cpu().numpy() < 0
+        assert float(dk[bb, hh][torch.from_numpy(dropped).to(dev)].abs().max()) == 0.0
+        live = np.isfinite(lse[bb, hh].double().cpu().numpy())
+        dv_sum = dv[bb, hh].double().sum(dim=0).cpu().numpy()
+        do_live = do[live].sum(axis=0)
+        assert np.linalg.norm(dv_sum - do_live) <= 2e-2 * max(np.linalg.norm(do_live), 1.0)
+        print(f"  head ({bb},{hh}): rows {rows.size} cols {cols.size} ok", flush=True)
+    del wl
+    torch.cuda.empty_cache()
