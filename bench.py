@@ -78,9 +78,11 @@ def measured_traffic(workload: str):
         return None
 
 
-def unmasked_pairs(spec: W.MaskSpec, H: int) -> int:
-    """U by per-column interval union (inclusion-exclusion over at most three intervals)."""
+def unmasked_pairs(spec: W.MaskSpec, H: int, rows=None) -> int:
+    """U by per-column interval union (inclusion-exclusion over at most three intervals), over all query
+    rows or over the row block rows = (a, b)."""
     N = spec.N
+    ra, rb = (0, N) if rows is None else rows
     j = np.arange(N, dtype=np.int64)
     zero = np.zeros(N, dtype=np.int64)
     total = 0
@@ -101,10 +103,11 @@ def unmasked_pairs(spec: W.MaskSpec, H: int) -> int:
             def meet(a, c):
                 return np.maximum(a[0], c[0]), np.minimum(a[1], c[1])
 
-            A, Bv, Cv = ivs
+            blk = (np.full(N, ra, np.int64), np.full(N, rb, np.int64))
+            A, Bv, Cv = (meet(x, blk) for x in ivs)
             union = ln(A) + ln(Bv) + ln(Cv) - ln(meet(A, Bv)) - ln(meet(A, Cv)) - ln(meet(Bv, Cv)) \
                 + ln(meet(meet(A, Bv), Cv))
-            total += (N * N - int(union.sum())) * (H if spec.Hm == 1 else 1)
+            total += ((rb - ra) * N - int(union.sum())) * (H if spec.Hm == 1 else 1)
     return total
 
 
@@ -212,6 +215,35 @@ def time_workload_compacted(fm, wl: Workload, steps: int, warmup: int):
         step()
     torch.cuda.synchronize()
     return time.perf_counter() - t0, ok
+
+
+def time_rows(fm, wl: Workload, a: int, b: int, steps: int, warmup: int):
+    """fm_fwd_rows + fm_bwd_rows of the query rows [a, b) against all keys: one rank's share under
+    context parallelism, at its real shape."""
+    import torch
+    q = wl.q[:, :, a:b].contiguous()
+    do = wl.do[:, :, a:b].contiguous()
+    bounds = fm.fm_tile_bounds(*wl.vecs, wl.B, wl.spec.Hm, wl.N) if wl.has_vecs else None
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, b - a), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(wl.k), torch.empty_like(wl.v)
+    ws = torch.empty(fm.fm_bwd_workspace_bytes(torch.bfloat16, wl.B, wl.H, b - a, wl.d), dtype=torch.uint8,
+                     device=q.device)
+
+    def step():
+        fm.fm_fwd_rows(q, wl.k, wl.v, a, *wl.vecs, bounds=bounds, causal=wl.spec.causal, scale=wl.scale, out=out,
+                       lse=lse)
+        fm.fm_bwd_rows(q, wl.k, wl.v, out, do, lse, a, *wl.vecs, bounds=bounds, causal=wl.spec.causal,
+                       scale=wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
 
 
 def cpu_baseline(wl: Workload, budget_heads: int, max_tokens: int):
@@ -323,6 +355,24 @@ def main():
             sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
                            "U": int(wl.U), "fwd_ms": round(float(p2[1]), 3), "bwd_ms": round(float(p2[2]), 3),
                            "bounds_ms": round(float(p2[0]), 4), "finite": ok2}
+        # one context-parallel rank's share at its real shape: the long-context workload over 8 ranks,
+        # each rank's contiguous 16384 query rows against all keys
+        del wl
+        torch.cuda.empty_cache()
+        wl = Workload("long_context_causal_document", dev)
+        ranks = 8
+        per = wl.N // ranks
+        cp = []
+        for r in range(ranks):
+            a, b = r * per, (r + 1) * per
+            t = time_rows(fm, wl, a, b, max(2, args.steps // 8), 1)
+            u = unmasked_pairs(wl.spec, wl.H, rows=(a, b))
+            cp.append({"rank": r, "rows": [a, b], "ms": round(t * 1e3, 3), "U": int(u),
+                       "TFLOP/s": round(14.0 * wl.d * u / t / 1e12, 2)})
+        ms = [c["ms"] for c in cp]
+        sweep["long_context_causal_document, context-parallel rank shares (8 ranks)"] = {
+            "ranks": cp, "max_ms": max(ms), "mean_ms": round(sum(ms) / len(ms), 3),
+            "imbalance_max_over_mean": round(max(ms) / (sum(ms) / len(ms)), 3)}
         del wl
         torch.cuda.empty_cache()
         wl = Workload("dpo_rm_causal_key_drop", dev)

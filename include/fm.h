@@ -107,6 +107,28 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
                  const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* One block of query rows against all keys: the unit of work of one rank under context parallelism,
+ * whose mask localisation is a zero-communication clip-shift-max on the boundary vectors that keeps the
+ * single-GPU kernel (FlashMask-3 summary, readmex.ai, the quoted abstract in the "in-depth insights"
+ * section). Here the kernels apply that shift to their own row indices: local query row i is global row
+ * q_off + i, and the vectors, the tile bounds and the causal rule (q_off + i < j) are read in global
+ * coordinates, so the caller passes the full vectors unchanged.
+ *   q, out, dout, dq: [B, H, Nq, d]; lse: float32 [B, H, Nq]; k, v, dk, dv: [B, H, Nk, d];
+ *   vectors: int32 [B, Hm, Nk] (values are global query rows); bounds from fm_tile_bounds(..., Nk, ...).
+ * out, lse and dq are exactly those rows of the whole problem; dk and dv are the contributions of these
+ * rows only (summing them over a partition of the rows gives the whole dk, dv). The workspace is
+ * fm_bwd_workspace_bytes(dtype, B, H, Nq, d). fm_fwd / fm_bwd are the case Nq = Nk = N, q_off = 0.
+ * Errors as fm_fwd / fm_bwd; also FM_ERR_INVALID for q_off < 0 or q_off + Nq > FM_MAX_N. */
+fm_status fm_fwd_rows(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int Nq, int Nk,
+                      int q_off, int d, const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                      const int32_t* ute, int Hm, const int32_t* bounds, int causal, float scale, void* out,
+                      float* lse, hipStream_t stream);
+fm_status fm_bwd_rows(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d,
+                      const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                      const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
 /* Key compaction for masks that drop whole key columns (per-head key dropping with compute reduced in
  * proportion to the keys kept: SCFA review, nubint.ai, "proposed method"). A column is dropped when it
  * is masked for every query row i in [0, N) (its causal rows, LT and UT together cover [0, N)). For each

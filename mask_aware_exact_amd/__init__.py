@@ -2,7 +2,8 @@
 
 Argument marshalling only: torch supplies device memory and the current stream, every step of the
 path runs in the HIP kernels behind the C ABI declared in include/fm.h. The entry points keep the C
-names: fm_tile_bounds, fm_fwd, fm_bwd, the key-compaction pair fm_compact_keys and fm_gather_rows
+names: fm_tile_bounds, fm_fwd, fm_bwd, their row-block forms fm_fwd_rows and fm_bwd_rows, the
+key-compaction pair fm_compact_keys and fm_gather_rows
 (plus fm_tile_classes, a test hook). There is no fallback:
 if libfm.so is missing or cannot be loaded, every call raises.
 """
@@ -21,8 +22,8 @@ FM_BF16, FM_F32 = 0, 1
 NONE, PARTIAL, FULL = 0, 1, 2
 
 EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_fwd",
-            "fm_bwd_workspace_bytes", "fm_bwd", "fm_tile_classes", "fm_compact_keys", "fm_gather_rows",
-            "fm_status_str")
+            "fm_bwd_workspace_bytes", "fm_bwd", "fm_fwd_rows", "fm_bwd_rows", "fm_tile_classes",
+            "fm_compact_keys", "fm_gather_rows", "fm_status_str")
 
 
 class FmError(RuntimeError):
@@ -59,6 +60,10 @@ def load_library(path: str = LIB_PATH):
     lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P, P, S, P]
     lib.fm_tile_classes.restype = I
     lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
+    lib.fm_fwd_rows.restype = I
+    lib.fm_fwd_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P]
+    lib.fm_bwd_rows.restype = I
+    lib.fm_bwd_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P, P, S, P]
     lib.fm_compact_keys.restype = I
     lib.fm_compact_keys.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P]
     lib.fm_gather_rows.restype = I
@@ -224,3 +229,47 @@ def fm_gather_rows(x, idx, y=None, stream=None):
     _check(lib.fm_gather_rows(_ptr(x), _dtype_code(x), B, H, N, d, _ptr(idx), idx.shape[1], _ptr(y),
                               _stream(stream)), "fm_gather_rows")
     return y
+
+
+def fm_fwd_rows(q, k, v, q_off: int, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False,
+                scale=None, out=None, lse=None, stream=None):
+    """(out, lse) for the query rows q_off .. q_off + Nq - 1 (q: [B, H, Nq, d]) against all keys
+    (k, v: [B, H, Nk, d]); vectors int32 [B, Hm, Nk] in global row coordinates."""
+    lib = load_library()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, bounds, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.fm_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, Nq, Nk, int(q_off), d,
+                           *[_ptr(x) for x in vecs], Hm, _ptr(bounds), int(bool(causal)), float(scale), _ptr(out),
+                           _ptr(lse), _stream(stream)), "fm_fwd_rows")
+    return out, lse
+
+
+def fm_bwd_rows(q, k, v, out, dout, lse, q_off: int, lts=None, lte=None, uts=None, ute=None, bounds=None,
+                causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of the row block: dq for its rows, dk / dv the contributions of its rows."""
+    lib = load_library()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, out, dout, lse, bounds, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fm_bwd_workspace_bytes(q.dtype, B, H, Nq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fm_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, Nq,
+                           Nk, int(q_off), d, *[_ptr(x) for x in vecs], Hm, _ptr(bounds), int(bool(causal)),
+                           float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                           _stream(stream)), "fm_bwd_rows")
+    return dq, dk, dv

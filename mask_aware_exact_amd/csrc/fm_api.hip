@@ -14,11 +14,11 @@ hipError_t launch_tile_classes(const int* bounds, int rows, int N, int causal, i
                                hipStream_t stream);
 hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
                       const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
-                      int N, int Hm, int causal, float scale, hipStream_t stream);
+                      int Nq, int Nk, int q_off, int Hm, int causal, float scale, hipStream_t stream);
 hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
-                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int N, int Hm,
-                      int causal, float scale, hipStream_t stream);
+                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
+                      int Nk, int q_off, int Hm, int causal, float scale, hipStream_t stream);
 int fwd_qblock();
 hipError_t launch_compact_keys(const int* lts, const int* lte, const int* uts, const int* ute, int rows, int N,
                                int causal, int* kidx, int* kpos, int* counts, int* lts2, int* lte2, int* uts2,
@@ -59,6 +59,12 @@ fm_status mask_args_ok(const int32_t* lts, const int32_t* lte, const int32_t* ut
 
 fm_status from_hip(hipError_t e) { return e == hipSuccess ? FM_OK : FM_ERR_LAUNCH; }
 
+// A row block [q_off, q_off + Nq) of a problem with Nk keys: both sizes in range and global row indices
+// inside int32 arithmetic.
+bool rows_ok(int B, int H, int Nq, int Nk, int q_off) {
+  return sizes_ok(B, H, Nq) && sizes_ok(B, H, Nk) && q_off >= 0 && (long long)q_off + Nq <= FM_MAX_N;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,18 +85,26 @@ fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* 
   return from_hip(fm::launch_tile_bounds(lts, lte, uts, ute, B * Hm, N, bounds, stream));
 }
 
-fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
-                 const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
-                 const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream) {
+fm_status fm_fwd_rows(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int Nq, int Nk,
+                      int q_off, int d, const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                      const int32_t* ute, int Hm, const int32_t* bounds, int causal, float scale, void* out,
+                      float* lse, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return FM_ERR_INVALID;
-  if (!sizes_ok(B, H, N) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
+  if (!rows_ok(B, H, Nq, Nk, q_off) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
   fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
   if (st != FM_OK) return st;
   st = dtype_d_ok(dtype, d);
   if (st != FM_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FM_ERR_INVALID;
-  return from_hip(fm::launch_fwd(dtype == FM_BF16, d, q, k, v, out, lse, lts, lte, uts, ute, bounds, B, H, N, Hm,
-                                 causal != 0, scale, stream));
+  return from_hip(fm::launch_fwd(dtype == FM_BF16, d, q, k, v, out, lse, lts, lte, uts, ute, bounds, B, H, Nq, Nk,
+                                 q_off, Hm, causal != 0, scale, stream));
+}
+
+fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
+                 const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                 const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream) {
+  return fm_fwd_rows(q, k, v, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, causal, scale, out, lse,
+                     stream);
 }
 
 size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d) {
@@ -99,14 +113,15 @@ size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d) {
   return round_up(rows * sizeof(float));
 }
 
-fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                 fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts, const int32_t* lte,
-                 const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds, int causal, float scale,
-                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+fm_status fm_bwd_rows(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d,
+                      const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                      const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return FM_ERR_INVALID;
-  if (!sizes_ok(B, H, N) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
+  if (!rows_ok(B, H, Nq, Nk, q_off) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
   fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
   if (st != FM_OK) return st;
   st = dtype_d_ok(dtype, d);
@@ -114,11 +129,19 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
   const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FM_ERR_INVALID;
-  const size_t need = fm_bwd_workspace_bytes(dtype, B, H, N, d);
+  const size_t need = fm_bwd_workspace_bytes(dtype, B, H, Nq, d);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FM_ERR_WORKSPACE;
   float* dd = static_cast<float*>(workspace);
   return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dd, lts, lte, uts, ute,
-                                 bounds, B, H, N, Hm, causal != 0, scale, stream));
+                                 bounds, B, H, Nq, Nk, q_off, Hm, causal != 0, scale, stream));
+}
+
+fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts, const int32_t* lte,
+                 const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds, int causal, float scale,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fm_bwd_rows(q, k, v, out, dout, lse, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, causal, scale,
+                     dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 fm_status fm_compact_keys(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int B,

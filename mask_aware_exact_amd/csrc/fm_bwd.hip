@@ -32,7 +32,9 @@ struct BwdArgs {
   const int* uts;
   const int* ute;
   const int* bounds;
-  int B, H, N, Hm;
+  int B, H, Hm;
+  int Nq, Nk;  // query rows and keys per head
+  int q_off;   // global index of query row 0: the mask and the causal rule see rows q_off + i
   int nkb;  // bounds entries per (b, hm) row
   int causal;
   float scale;
@@ -74,23 +76,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int l32 = lane & 31;
 
   const int BH = a.B * a.H;
-  const int nq = (a.N + BR - 1) / BR;
+  const int nq = (a.Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
   const int qt = nq - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) query tiles first
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
-  const int N = a.N;
+  const int Nq = a.Nq, N = a.Nk;  // N: keys
   const int r0 = qt * BR;
-  const int r1 = min(N, r0 + BR);
+  const int r1 = min(Nq, r0 + BR);
   const int row = r0 + wave * 32 + l32;  // this lane's query row
+  const int g0 = a.q_off + r0, g1 = a.q_off + r1;  // the tile's rows in the mask's coordinates
+  const int gend = a.q_off + Nq;
 
-  const size_t head = (size_t)bh * N * D;
-  const T* __restrict__ qg = static_cast<const T*>(a.q) + head;
-  const T* __restrict__ kg = static_cast<const T*>(a.k) + head;
-  const T* __restrict__ vg = static_cast<const T*>(a.v) + head;
-  const T* __restrict__ og = static_cast<const T*>(a.out) + head;
-  const T* __restrict__ dog = static_cast<const T*>(a.dout) + head;
+  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * N * D;
+  const T* __restrict__ qg = static_cast<const T*>(a.q) + qhead;
+  const T* __restrict__ kg = static_cast<const T*>(a.k) + khead;
+  const T* __restrict__ vg = static_cast<const T*>(a.v) + khead;
+  const T* __restrict__ og = static_cast<const T*>(a.out) + qhead;
+  const T* __restrict__ dog = static_cast<const T*>(a.dout) + qhead;
   const size_t vrow = ((size_t)b * a.Hm + hm) * N;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
   const bool has_lt = a.lts != nullptr;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   float part = 0.f;
 #pragma unroll
   for (int c = 0; c < Tr::NQF; ++c) {
-    if (row < N) {
+    if (row < Nq) {
       const size_t e = (size_t)row * D + c * M::KW + g * M::E;
       qf[c] = load_kcontig_frag<T>(qg + e);
       df[c] = load_kcontig_frag<T>(dog + e);
@@ -121,10 +125,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   const float Di = part + __shfl_xor(part, 32, 64);
   float lse2 = INFINITY;  // rows past N or without any unmasked key: exp(S - lse) = 0
-  if (row < N) {
-    const float l = a.lse[(size_t)bh * N + row];
+  if (row < Nq) {
+    const float l = a.lse[(size_t)bh * Nq + row];
     lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
-    if (g == 0) a.dd[(size_t)bh * N + row] = Di;
+    if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;
   }
 
   f32x16 acc[Tr::NDB];
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   const int nkt = (N + BC - 1) / BC;
-  const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
+  const int kt_end = causal ? min(nkt, (g1 - 1) / BC + 1) : nkt;
 
   // Next tile: K / V (bf16: straight into LDS buffer `dst`; float: into staging registers) and the
   // tile's mask vectors (registers).
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   auto class_of = [&](int t) {
     const TileBounds bt = merged_bounds(brow, t, t + 1, N);
-    return classify_tile(r0, r1, t * BC, min(N, t * BC + BC), bt, causal);
+    return classify_tile(g0, g1, t * BC, min(N, t * BC + BC), bt, causal);
   };
   TileWindow win = empty_window();
   int kt = next_live_tile(win, 0, kt_end, class_of, lane);
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
     // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0 (masked scores set to -inf).
     if (need_mask) {
-      tile_column_words(cw_lds[wave], vec_lds[buf], r0 + wave * 32, c0, N, causal, has_lt, has_ut, lane);
+      tile_column_words(cw_lds[wave], vec_lds[buf], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut, lane);
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -266,8 +270,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // dq = scale * dQ^T for this lane's row.
-  if (row < N) {
-    T* dqg = static_cast<T*>(a.dq) + head + (size_t)row * D;
+  if (row < Nq) {
+    T* dqg = static_cast<T*>(a.dq) + qhead + (size_t)row * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
@@ -338,19 +342,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
-  const int N = a.N;
+  const int N = a.Nk, Nq = a.Nq, qoff = a.q_off;  // N: keys
   const int c0 = kt * BC;
   const int c1 = min(N, c0 + BC);
   const int jl = kgrp * 32 + l32;  // this lane's key column inside the tile
   const int j = c0 + jl;
 
-  const size_t head = (size_t)bh * N * D;
-  const bf16* __restrict__ qg = static_cast<const bf16*>(a.q) + head;
-  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + head;
-  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + head;
-  const bf16* __restrict__ dog = static_cast<const bf16*>(a.dout) + head;
-  const float* __restrict__ lseg = a.lse + (size_t)bh * N;
-  const float* __restrict__ ddg = a.dd + (size_t)bh * N;
+  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * N * D;
+  const bf16* __restrict__ qg = static_cast<const bf16*>(a.q) + qhead;
+  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + khead;
+  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + khead;
+  const bf16* __restrict__ dog = static_cast<const bf16*>(a.dout) + qhead;
+  const float* __restrict__ lseg = a.lse + (size_t)bh * Nq;
+  const float* __restrict__ ddg = a.dd + (size_t)bh * Nq;
   const size_t vrow = ((size_t)b * a.Hm + hm) * N;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
   const bool has_lt = a.lts != nullptr;
@@ -384,9 +388,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   for (int db = 0; db < Tr::NDB; ++db) acc[db] = zero16();
 
   const TileBounds bnd = merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N);
-  const int nq = (N + BR - 1) / BR;
-  const int qt_begin = causal ? c0 / BR : 0;
-  auto class_of = [&](int qt) { return classify_tile(qt * BR, min(N, qt * BR + BR), c0, c1, bnd, causal); };
+  const int nq = (Nq + BR - 1) / BR;
+  const int qt_begin = causal ? max(0, c0 - qoff) / BR : 0;
+  auto class_of = [&](int qt) {
+    return classify_tile(qoff + qt * BR, qoff + min(Nq, qt * BR + BR), c0, c1, bnd, causal);
+  };
 
   // Next query tile: Q and dO straight into their ring slots (direct global-to-LDS copies; rows past N
   // read row N - 1, which gets lse = +inf below and so contributes nothing), lse and D into registers.
@@ -396,17 +402,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     const int q0 = qt * BR;
     if (tid < BR) {
       l_row = q0 + tid;
-      const int i = min(l_row, N - 1);
+      const int i = min(l_row, Nq - 1);
       lr = lseg[i];
       ddr = ddg[i];
     }
-    copy_tile_async<D, BR, 8>(q_lds + qslot * TILE, qg, q0, N, wave, lane);
-    copy_tile_async<D, BR, 8>(do_lds + dslot * TILE, dog, q0, N, wave, lane);
+    copy_tile_async<D, BR, 8>(q_lds + qslot * TILE, qg, q0, Nq, wave, lane);
+    copy_tile_async<D, BR, 8>(do_lds + dslot * TILE, dog, q0, Nq, wave, lane);
   };
   auto stash = [&](int ds) {
     if (tid < BR) {
       // rows past N and rows without any unmasked key (lse = -inf) get +inf: exp(S - lse) = 0 for them
-      const float l = (l_row >= N || lr == -INFINITY) ? INFINITY : lr;
+      const float l = (l_row >= Nq || lr == -INFINITY) ? INFINITY : lr;
       lse_lds[ds][tid] = l * LOG2E;
       dd_lds[ds][tid] = ddr;
     }
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
   while (qt < nq) {
     const int q0 = qt * BR;
-    const bool need_mask = window_partial(win, qt) || (q0 + BR > N) || (c0 + BC > N);
+    const bool need_mask = window_partial(win, qt) || (q0 + BR > Nq) || (c0 + BC > N);
     stash(ds);
     __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();  // (A) the tile is in LDS; every wave is past the previous tile's work
@@ -460,7 +466,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
       if (need_mask) {
-        const uint64_t mbits = masked_row_bits(q0, j, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
+        const uint64_t mbits =
+            masked_row_bits(qoff + q0, j, qoff + Nq, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
         const uint32_t mlo = (uint32_t)(mbits >> (4 * g)), mhi = (uint32_t)(mbits >> (32 + 4 * g));
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
   // dV = dV^T (role 0) or dK = scale * dK^T (role 1) for this lane's key column, all of d.
   if (j < N) {
-    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + head + (size_t)j * D;
+    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + khead + (size_t)j * D;
     const float mul = role == 0 ? 1.f : a.scale;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
@@ -587,16 +594,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
-  const int N = a.N;
+  const int N = a.Nk, Nq = a.Nq, qoff = a.q_off;  // N: keys
   const int c0 = kt * BC;
   const int c1 = min(N, c0 + BC);
   const int j = c0 + wave * 32 + l32;
 
-  const size_t head = (size_t)bh * N * D;
-  const float* __restrict__ qg = static_cast<const float*>(a.q) + head;
-  const float* __restrict__ kg = static_cast<const float*>(a.k) + head;
-  const float* __restrict__ vg = static_cast<const float*>(a.v) + head;
-  const float* __restrict__ dog = static_cast<const float*>(a.dout) + head;
+  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * N * D;
+  const float* __restrict__ qg = static_cast<const float*>(a.q) + qhead;
+  const float* __restrict__ kg = static_cast<const float*>(a.k) + khead;
+  const float* __restrict__ vg = static_cast<const float*>(a.v) + khead;
+  const float* __restrict__ dog = static_cast<const float*>(a.dout) + qhead;
   const size_t vrow = ((size_t)b * a.Hm + hm) * N;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
   const bool has_lt = a.lts != nullptr;
@@ -622,21 +629,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
     dv[db] = zero16();
   }
   const TileBounds bnd = merged_bounds(brow, kt * (BC / KBLOCK), min(a.nkb, (kt + 1) * (BC / KBLOCK)), N);
-  const int nq = (N + BR - 1) / BR;
-  for (int qt = causal ? c0 / BR : 0; qt < nq; ++qt) {
+  const int nq = (Nq + BR - 1) / BR;
+  for (int qt = causal ? max(0, c0 - qoff) / BR : 0; qt < nq; ++qt) {
     const int q0 = qt * BR;
-    const int q1 = min(N, q0 + BR);
-    const int cls = classify_tile(q0, q1, c0, c1, bnd, causal);
+    const int q1 = min(Nq, q0 + BR);
+    const int cls = classify_tile(qoff + q0, qoff + q1, c0, c1, bnd, causal);
     if (cls == CLS_FULL) continue;
     const bool need_mask = (cls == CLS_PARTIAL) || (q1 - q0 < BR) || (c1 - c0 < BC);
     __syncthreads();
-    load_tile<float, BR, D, PITCH, Tr::NT>(q_lds, qg, q0, N, tid);
-    load_tile<float, BR, D, PITCH, Tr::NT>(do_lds, dog, q0, N, tid);
+    load_tile<float, BR, D, PITCH, Tr::NT>(q_lds, qg, q0, Nq, tid);
+    load_tile<float, BR, D, PITCH, Tr::NT>(do_lds, dog, q0, Nq, tid);
     if (tid < BR) {
       const int i = q0 + tid;
-      const float l = i < N ? a.lse[(size_t)bh * N + i] : INFINITY;
+      const float l = i < Nq ? a.lse[(size_t)bh * Nq + i] : INFINITY;
       lse_lds[tid] = ((l == -INFINITY) ? INFINITY : l) * LOG2E;
-      dd_lds[tid] = i < N ? a.dd[(size_t)bh * N + i] : 0.f;
+      dd_lds[tid] = i < Nq ? a.dd[(size_t)bh * Nq + i] : 0.f;
     }
     __syncthreads();
     f32x16 s = zero16(), dp = zero16();
@@ -650,8 +657,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
       const int il = 8 * (r >> 2) + 4 * g + (r & 3);
       const int i = q0 + il;
       float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - lse_lds[il]);
-      const bool msk = need_mask &
-                       ((i >= N) | (j >= N) | masked_elem(i, j, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute));
+      const bool msk = need_mask & ((i >= Nq) | (j >= N) |
+                                    masked_elem(qoff + i, j, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute));
       p = msk ? 0.f : p;
       s[r] = p;
       dp[r] = p * (dp[r] - dd_lds[il]);
@@ -666,8 +673,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
     }
   }
   if (j < N) {
-    float* dkg = static_cast<float*>(a.dk) + head + (size_t)j * D;
-    float* dvg = static_cast<float*>(a.dv) + head + (size_t)j * D;
+    float* dkg = static_cast<float*>(a.dk) + khead + (size_t)j * D;
+    float* dvg = static_cast<float*>(a.dv) + khead + (size_t)j * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
@@ -690,11 +697,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
-  const long nq = (a.N + DqTraits<T, D>::BR - 1) / DqTraits<T, D>::BR;
+  const long nq = (a.Nq + DqTraits<T, D>::BR - 1) / DqTraits<T, D>::BR;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)(nq * a.B * a.H)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long nkt = (a.N + 127) / 128;
+  const long nkt = (a.Nk + 127) / 128;
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)(nkt * a.B * a.H)), dim3(512), 0, stream, a);
   } else {
@@ -705,14 +712,15 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
 
 hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
-                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int N, int Hm,
-                      int causal, float scale, hipStream_t stream) {
+                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
+                      int Nk, int q_off, int Hm, int causal, float scale, hipStream_t stream) {
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.dd = dd;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
-  a.B = B; a.H = H; a.N = N; a.Hm = Hm;
-  a.nkb = (N + KBLOCK - 1) / KBLOCK;
+  a.B = B; a.H = H; a.Hm = Hm;
+  a.Nq = Nq; a.Nk = Nk; a.q_off = q_off;
+  a.nkb = (Nk + KBLOCK - 1) / KBLOCK;
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * LOG2E;

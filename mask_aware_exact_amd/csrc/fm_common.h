@@ -133,14 +133,15 @@ __device__ __forceinline__ uint64_t row_span_bits(int s, int e, int q0) {
   return below_z & ~below_a;
 }
 
-// Masked rows among q0 .. q0 + 63 for key column j (rows and columns at or past N count as masked).
-__device__ __forceinline__ uint64_t masked_row_bits(int q0, int j, int N, bool causal, bool has_lt, bool has_ut,
-                                                    int lts, int lte, int uts, int ute) {
-  uint64_t m = row_span_bits(N, 0x7fffffff, q0);
+// Masked rows among q0 .. q0 + 63 for key column j. Rows are global query indices (the mask's own
+// coordinates); rows at or past row_end and columns at or past nk count as masked.
+__device__ __forceinline__ uint64_t masked_row_bits(int q0, int j, int row_end, int nk, bool causal, bool has_lt,
+                                                    bool has_ut, int lts, int lte, int uts, int ute) {
+  uint64_t m = row_span_bits(row_end, 0x7fffffff, q0);
   m |= causal ? row_span_bits(0, j, q0) : 0ull;
   m |= has_lt ? row_span_bits(lts, lte, q0) : 0ull;
   m |= has_ut ? row_span_bits(uts, ute, q0) : 0ull;
-  return j >= N ? ~0ull : m;
+  return j >= nk ? ~0ull : m;
 }
 
 // The same for the 32 rows q0 .. q0 + 31.
@@ -152,13 +153,13 @@ __device__ __forceinline__ uint32_t row_span_bits32(int s, int e, int q0) {
   return below_z & ~below_a;
 }
 
-__device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int N, bool causal, bool has_lt, bool has_ut,
-                                                      int lts, int lte, int uts, int ute) {
-  uint32_t m = row_span_bits32(N, 0x7fffffff, q0);
+__device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int row_end, int nk, bool causal, bool has_lt,
+                                                      bool has_ut, int lts, int lte, int uts, int ute) {
+  uint32_t m = row_span_bits32(row_end, 0x7fffffff, q0);
   m |= causal ? row_span_bits32(0, j, q0) : 0u;
   m |= has_lt ? row_span_bits32(lts, lte, q0) : 0u;
   m |= has_ut ? row_span_bits32(uts, ute, q0) : 0u;
-  return j >= N ? ~0u : m;
+  return j >= nk ? ~0u : m;
 }
 
 // Masks of a 64-key tile in the S^T layout (rows = keys in two 32-key blocks, columns = a wave's 32
@@ -166,10 +167,10 @@ __device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int N, bool
 // q0 .. q0 + 31 and stores it in the wave's own 64-word LDS row; the wave then reads back the words of
 // the columns its registers hold. LDS operations of one wave run in order, and the wave-scope fences
 // keep the compiler from moving the read-back above the store.
-__device__ __forceinline__ void tile_column_words(uint32_t* cw, const i32x4* vec, int q0, int c0, int N, bool causal,
-                                                  bool has_lt, bool has_ut, int lane) {
+__device__ __forceinline__ void tile_column_words(uint32_t* cw, const i32x4* vec, int q0, int c0, int row_end, int nk,
+                                                  bool causal, bool has_lt, bool has_ut, int lane) {
   const i32x4 mv = vec[lane];
-  cw[lane] = masked_row_bits32(q0, c0 + lane, N, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
+  cw[lane] = masked_row_bits32(q0, c0 + lane, row_end, nk, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -38,7 +38,9 @@ struct FwdArgs {
   const int* uts;
   const int* ute;
   const int* bounds;
-  int B, H, N, Hm;
+  int B, H, Hm;
+  int Nq, Nk;  // query rows and keys per head
+  int q_off;   // global index of query row 0: the mask and the causal rule see rows q_off + i
   int nq;   // query tiles per head
   int nkb;  // bounds entries per (b, hm) row
   int causal;
@@ -90,15 +92,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
-  const int N = a.N;
+  const int Nq = a.Nq, N = a.Nk;  // N: keys
   const int r0 = qt * BR;
-  const int r1 = min(N, r0 + BR);
+  const int r1 = min(Nq, r0 + BR);
   const int row = r0 + wave * 32 + l32;  // this lane's query row
+  const int g0 = a.q_off + r0, g1 = a.q_off + r1;  // the tile's rows in the mask's coordinates
+  const int gend = a.q_off + Nq;
 
-  const size_t head = (size_t)bh * N * D;
-  const T* __restrict__ qg = static_cast<const T*>(a.q) + head;
-  const T* __restrict__ kg = static_cast<const T*>(a.k) + head;
-  const T* __restrict__ vg = static_cast<const T*>(a.v) + head;
+  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * N * D;
+  const T* __restrict__ qg = static_cast<const T*>(a.q) + qhead;
+  const T* __restrict__ kg = static_cast<const T*>(a.k) + khead;
+  const T* __restrict__ vg = static_cast<const T*>(a.v) + khead;
   const size_t vrow = ((size_t)b * a.Hm + hm) * N;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + ((size_t)b * a.Hm + hm) * a.nkb * 8;
   const bool has_lt = a.lts != nullptr;
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   typename M::frag qf[Tr::NQF];
 #pragma unroll
   for (int c = 0; c < Tr::NQF; ++c) {
-    if (row < N) {
+    if (row < Nq) {
       qf[c] = load_kcontig_frag<T>(qg + (size_t)row * D + c * M::KW + g * M::E);
     } else {
       qf[c] = typename M::frag{};
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   float l_run = 0.f;        // this lane's share of the denominator, relative to m_ref
 
   const int nkt = (N + BC - 1) / BC;
-  const int kt_end = causal ? min(nkt, (r1 - 1) / BC + 1) : nkt;
+  const int kt_end = causal ? min(nkt, (g1 - 1) / BC + 1) : nkt;
 
   // Next tile: K / V (bf16: straight into LDS buffer `dst`; float: into staging registers) and the
   // tile's mask vectors (registers).
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   auto class_of = [&](int t) {
     const TileBounds bt = merged_bounds(brow, t, t + 1, N);
-    return classify_tile(r0, r1, t * BC, min(N, t * BC + BC), bt, causal);
+    return classify_tile(g0, g1, t * BC, min(N, t * BC + BC), bt, causal);
   };
   TileWindow win = empty_window();
   int kt = next_live_tile(win, 0, kt_end, class_of, lane);
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
     float mx = -INFINITY;
     if (need_mask) {
-      tile_column_words(cw_lds[wave], vec_lds[buf], r0 + wave * 32, c0, N, causal, has_lt, has_ut, lane);
+      tile_column_words(cw_lds[wave], vec_lds[buf], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut, lane);
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -287,10 +291,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   // Epilogue: out = O / l, lse = m_ref * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (row < N) {
+  if (row < Nq) {
     const bool dead = !(l_tot > 0.f);
     const float inv = dead ? 0.f : 1.f / l_tot;
-    T* og = static_cast<T*>(a.out) + head + (size_t)row * D;
+    T* og = static_cast<T*>(a.out) + qhead + (size_t)row * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (g == 0) a.lse[(size_t)bh * N + row] = dead ? -INFINITY : m_ref * LN2 + logf(l_tot);
+    if (g == 0) a.lse[(size_t)bh * Nq + row] = dead ? -INFINITY : m_ref * LN2 + logf(l_tot);
   }
 }
 
@@ -324,13 +328,14 @@ int fwd_qblock() { return 128; }
 
 hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
                       const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
-                      int N, int Hm, int causal, float scale, hipStream_t stream) {
+                      int Nq, int Nk, int q_off, int Hm, int causal, float scale, hipStream_t stream) {
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
   a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
-  a.B = B; a.H = H; a.N = N; a.Hm = Hm;
-  a.nq = (N + 127) / 128;
-  a.nkb = (N + KBLOCK - 1) / KBLOCK;
+  a.B = B; a.H = H; a.Hm = Hm;
+  a.Nq = Nq; a.Nk = Nk; a.q_off = q_off;
+  a.nq = (Nq + 127) / 128;
+  a.nkb = (Nk + KBLOCK - 1) / KBLOCK;
   a.causal = causal;
   a.scale_log2 = scale * LOG2E;
   if (bf16_in) return d == 64 ? launch_fwd_t<bf16, 64>(a, stream) : launch_fwd_t<bf16, 128>(a, stream);

@@ -91,6 +91,35 @@ def fwd_bwd_head(q, k, v, do, vecs, causal, scale, row_block=None):
     return out, lse, dq, dk, dv
 
 
+def fwd_bwd_rows_head(q_rows, k, v, do_rows, vecs, causal, scale, q_off, row_block=None):
+    """Query rows q_off .. q_off + Nq - 1 of one head against all Nk keys, the mask read in the global row
+    coordinates of the vectors (the unit of work of one rank under context parallelism, FlashMask-3
+    summary, readmex.ai). q_rows, do_rows [Nq, d]; k, v [Nk, d]; vecs 1-D over the Nk columns or None.
+
+    Returns out [Nq, d], lse [Nq], dq [Nq, d] of those rows and the contributions of those rows to
+    dk, dv [Nk, d]."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    do_rows = np.asarray(do_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Nq, d = q_rows.shape
+    Nk = k.shape[0]
+    rb = row_block or _row_block(max(Nq, Nk))
+    out = np.zeros((Nq, d))
+    lse = np.full(Nq, -np.inf)
+    dq = np.zeros((Nq, d))
+    dk = np.zeros((Nk, d))
+    dv = np.zeros((Nk, d))
+    for r0 in range(0, Nq, rb):
+        r1 = min(Nq, r0 + rb)
+        masked = dense_masked_rows(*vecs, causal, Nk, q_off + r0, q_off + r1)
+        res = attend_rows(q_rows[r0:r1], k, v, do_rows[r0:r1], masked, scale)
+        out[r0:r1], lse[r0:r1], dq[r0:r1] = res["out"], res["lse"], res["dq"]
+        dk += scale * (res["dS"].T @ q_rows[r0:r1])
+        dv += res["P"].T @ do_rows[r0:r1]
+    return out, lse, dq, dk, dv
+
+
 def fwd_bwd(q, k, v, do, vectors, causal, scale, Hm, heads=None, workers=None):
     """Forward and backward over [B, H, N, d] arrays; vectors are the four [B, Hm, N] arrays or None.
 

@@ -160,3 +160,21 @@ def test_gather_validation(lib):
     assert _gather(lib, dtype=5) == fm.FM_ERR_UNSUPPORTED
     assert _gather(lib, y=P(0x200004)) == fm.FM_ERR_INVALID       # misaligned
     assert _gather(lib, H=0) == fm.FM_ERR_INVALID
+
+
+def test_rows_validation(lib):
+    # (q, k, v, dtype, B, H, Nq, Nk, q_off, d, lts, lte, uts, ute, Hm, bounds, causal, scale, out, lse, stream)
+    def fwd_rows(Nq=100, Nk=100, q_off=0):
+        return lib.fm_fwd_rows(A, A, A, fm.FM_BF16, 1, 2, Nq, Nk, q_off, 64, None, None, None, None, 1, None, 1,
+                               0.125, B_, B_, None)
+    assert fwd_rows(q_off=-1) == fm.FM_ERR_INVALID
+    assert fwd_rows(Nk=0) == fm.FM_ERR_INVALID
+    assert fwd_rows(Nq=0) == fm.FM_ERR_INVALID
+    assert fwd_rows(q_off=(1 << 24) - 50) == fm.FM_ERR_INVALID    # rows past FM_MAX_N
+    ws = lib.fm_bwd_workspace_bytes(fm.FM_BF16, 1, 2, 100, 64)
+
+    def bwd_rows(q_off=0, wsb=ws):
+        return lib.fm_bwd_rows(A, A, A, A, A, A, fm.FM_BF16, 1, 2, 100, 100, q_off, 64, None, None, None, None, 1,
+                               None, 1, 0.125, B_, B_, B_, A, wsb, None)
+    assert bwd_rows(q_off=-3) == fm.FM_ERR_INVALID
+    assert bwd_rows(wsb=ws - 256) == fm.FM_ERR_WORKSPACE
