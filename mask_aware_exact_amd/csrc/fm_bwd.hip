@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
+    interleave_reads<4 * Tr::NQF, 4 * Tr::NQF, 2>();
     __builtin_amdgcn_s_setprio(0);
     // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0 (masked scores set to -inf).
     if (need_mask) {
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
+    interleave_reads<2 * Tr::TPB * Tr::NDB, 4 * Tr::TPB * Tr::NDB, 4>();
     __builtin_amdgcn_s_setprio(0);
     kt = kt_next;
     buf ^= 1;
@@ -431,6 +433,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) acc[db] = M::mma(crd.read(qb, t, db), sf, acc[db]);
     }
+    interleave_reads<4 * Tr::NDB, 8 * Tr::NDB, 4>();
   };
 
   TileWindow win = empty_window();
@@ -464,6 +467,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(qb, ib, c), xf[c], x[ib]);
       }
+      interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
       __builtin_amdgcn_s_setprio(0);
       if (need_mask) {
         const uint64_t mbits =
@@ -503,6 +507,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
       }
+      interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
     }
     __syncthreads();  // (B) P is in LDS
 
@@ -520,6 +525,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < Tr::NDB; ++db) acc[db] = M::mma(crd.read(dob, t, db), pf, acc[db]);
       }
+      interleave_reads<4 * Tr::NDB, 8 * Tr::NDB, 4>();
       __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll

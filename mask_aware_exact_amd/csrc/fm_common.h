@@ -278,6 +278,19 @@ __device__ __forceinline__ float acc_frag<float>(const f32x16& acc, int t) {
   return acc[t];
 }
 
+// Scheduling hint for a block of NM matrix products fed by NR LDS reads: LEAD reads first, then each
+// product followed by its share of the remaining reads, so that the reads stay a few products ahead
+// instead of being issued all at once. Must sit at the end of the block (same basic block).
+template <int NM, int NR, int LEAD>
+__device__ __forceinline__ void interleave_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, (NR - LEAD + NM - 1) / NM, 0);
+  }
+}
+
 // ------------------------------------------------------------------ swizzled bf16 tiles
 // A bf16 tile with rows of D elements (D * 2 bytes, unpadded) stores 16-byte chunk c of row r at chunk
 // position c ^ swz_key<D>(r). With 64 LDS banks of 4 bytes this makes both access patterns of the kernels

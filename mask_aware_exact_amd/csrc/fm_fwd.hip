@@ -217,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(load_kcontig_frag<T>(krow + c * M::KW), qf[c], s[jb]);
       }
     }
+    interleave_reads<2 * Tr::NQF, 2 * Tr::NQF, 2>();
 
     __builtin_amdgcn_s_setprio(0);
     // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
@@ -284,6 +285,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
       }
     }
+    interleave_reads<2 * Tr::TPB * Tr::NDB, 4 * Tr::TPB * Tr::NDB, 4>();
     __builtin_amdgcn_s_setprio(0);
     kt = kt_next;
     buf ^= 1;
