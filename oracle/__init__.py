@@ -14,5 +14,6 @@ Modules:
   tiles     per-key-tile min/max of the four vectors and the FULL/PARTIAL/NONE tile rule
   attention fp64 forward/backward (row-blocked), brute force for tiny cases, one-row/one-column probes
   compact   removal of the key columns masked for every row, and the compacted problem's mask
+  schedule  longest-first order of the work units by their count of tiles that are not fully masked
 """
-from . import masks, tiles, attention, compact  # noqa: F401
+from . import masks, tiles, attention, compact, schedule  # noqa: F401
