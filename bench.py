@@ -1,14 +1,17 @@
 """Benchmark: column-wise-mask (FlashMask) attention forward + backward on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input:
-fm_tile_bounds -> fm_fwd -> fm_bwd. The metric counts only unmasked FLOPs:
+fm_tile_bounds -> fm_fwd -> fm_bwd (with --schedule, fm_tile_schedule before fm_fwd and both kernels
+launched in its order). The metric counts only unmasked FLOPs:
     FLOP per step = 14 * d * U   (forward 4 d U: Q K^T and P V; backward 10 d U: the S recompute,
                                   dP, dV, dK and dQ products), U = unmasked (query, key) pairs.
 The default workload is the long-context configuration with a causal document mask (B=1, H=8,
 N=131072, d=128, bf16; document lengths log-uniform in [1K, 32K]), the largest head-dim-128 workload.
 
 Prints one JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --no-cpu-baseline,
---sweep (also time the other head-dim-128 workloads, a few steps each, reported under "sweep"),
+--schedule (launch in the longest-first order of fm_tile_schedule, computed inside each step),
+--sweep (also time the other head-dim-128 workloads, a few steps each, with and without the schedule,
+reported under "sweep"),
 --copy-calibration (after timing, one 1 GiB device-to-device copy, the reference kernel for scaling
 hardware byte counters in profiling runs).
 """
@@ -135,11 +138,15 @@ class Workload:
         self.flop = self.flop_fwd + self.flop_bwd
 
 
-def time_workload(fm, wl: Workload, steps: int, warmup: int):
+def time_workload(fm, wl: Workload, steps: int, warmup: int, use_sched: bool = False):
+    """One step = fm_tile_bounds (when the mask has vectors), fm_tile_schedule (longest-first dispatch
+    order, only with use_sched), fm_fwd, fm_bwd; all of it timed. Returns the wall time of the
+    timed steps, the mean per-part milliseconds (bounds, schedule, fwd, bwd) and a finiteness flag."""
     import torch
     dev = wl.q.device
     stream = torch.cuda.current_stream(dev)
     bounds = torch.empty(fm.fm_bounds_elems(wl.B, wl.spec.Hm, wl.N) or 8, dtype=torch.int32, device=dev)
+    sched_buf = torch.empty(fm.fm_schedule_elems(wl.B, wl.spec.Hm, wl.N, wl.N), dtype=torch.int32, device=dev)
     out = torch.empty_like(wl.q)
     lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
@@ -154,26 +161,31 @@ def time_workload(fm, wl: Workload, steps: int, warmup: int):
             b = fm.fm_tile_bounds(*wl.vecs, wl.B, wl.spec.Hm, wl.N, bounds=bounds)
         if evs is not None:
             evs[1].record(stream)
-        fm.fm_fwd(wl.q, wl.k, wl.v, *wl.vecs, bounds=b, causal=wl.spec.causal, scale=wl.scale, out=out, lse=lse)
+        sc = None
+        if use_sched:
+            sc = fm.fm_tile_schedule(b, wl.B, wl.spec.Hm, wl.N, wl.N, wl.spec.causal, sched=sched_buf)
         if evs is not None:
             evs[2].record(stream)
-        fm.fm_bwd(wl.q, wl.k, wl.v, out, wl.do, lse, *wl.vecs, bounds=b, causal=wl.spec.causal, scale=wl.scale,
-                  dq=dq, dk=dk, dv=dv, workspace=ws)
+        fm.fm_fwd(wl.q, wl.k, wl.v, *wl.vecs, bounds=b, sched=sc, causal=wl.spec.causal, scale=wl.scale, out=out,
+                  lse=lse)
         if evs is not None:
             evs[3].record(stream)
+        fm.fm_bwd(wl.q, wl.k, wl.v, out, wl.do, lse, *wl.vecs, bounds=b, sched=sc, causal=wl.spec.causal,
+                  scale=wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if evs is not None:
+            evs[4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    parts = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                      for e in events])  # ms
+    parts = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])  # ms
     ok = bool(torch.isfinite(out.float()).all() and torch.isfinite(dq.float()).all()
               and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all())
     return wall, parts.mean(axis=0), ok
@@ -283,6 +295,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--schedule", action="store_true",
+                    help="compute the longest-first dispatch schedule each step and launch in its order")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -300,10 +314,11 @@ def main():
     torch.cuda.set_device(dev)
 
     wl = Workload(args.workload, dev)
-    wall, parts_ms, ok = time_workload(fm, wl, args.steps, args.warmup)
+    use_sched = args.schedule
+    wall, parts_ms, ok = time_workload(fm, wl, args.steps, args.warmup, use_sched)
     ms_per_step = wall * 1e3 / args.steps
     tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
-    bwd_ms = float(parts_ms[2])
+    bwd_ms = float(parts_ms[3])
     bwd_tflops = wl.flop_bwd / (bwd_ms * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
@@ -322,9 +337,11 @@ def main():
                    "causal": bool(wl.spec.causal), "unmasked_pairs": int(wl.U),
                    "flop_per_step": wl.flop, "flop_formula": "14*d*U"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "parts_ms": {"fm_tile_bounds": round(float(parts_ms[0]), 4), "fm_fwd": round(float(parts_ms[1]), 4),
+        "schedule": "longest-first" if use_sched else "default order",
+        "parts_ms": {"fm_tile_bounds": round(float(parts_ms[0]), 4),
+                     "fm_tile_schedule": round(float(parts_ms[1]), 4), "fm_fwd": round(float(parts_ms[2]), 4),
                      "fm_bwd": round(bwd_ms, 4)},
-        "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[1] * 1e-3) / 1e12, 2),
+        "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[2] * 1e-3) / 1e12, 2),
                          "fm_bwd": round(bwd_tflops, 2)},
         "finite_outputs": ok,
         "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_dq_kernel then bwd_dkdv_pair_kernel)",
@@ -350,11 +367,18 @@ def main():
             del wl
             torch.cuda.empty_cache()
             wl = Workload(name, dev)
-            w2, p2, ok2 = time_workload(fm, wl, max(3, args.steps // 4), 1)
-            ms = w2 * 1e3 / max(3, args.steps // 4)
+            n = max(3, args.steps // 4)
+            w2, p2, ok2 = time_workload(fm, wl, n, 1, use_sched)
+            w0, p0, _ = time_workload(fm, wl, n, 1, not use_sched)
+            ms = w2 * 1e3 / n
             sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
-                           "U": int(wl.U), "fwd_ms": round(float(p2[1]), 3), "bwd_ms": round(float(p2[2]), 3),
-                           "bounds_ms": round(float(p2[0]), 4), "finite": ok2}
+                           "U": int(wl.U), "fwd_ms": round(float(p2[2]), 3), "bwd_ms": round(float(p2[3]), 3),
+                           "bounds_ms": round(float(p2[0]), 4), "schedule_ms": round(float(p2[1]), 4),
+                           "finite": ok2,
+                           ("ms_per_step_default_order" if use_sched else "ms_per_step_longest_first"):
+                               round(w0 * 1e3 / n, 3),
+                           ("fwd_bwd_ms_default_order" if use_sched else "fwd_bwd_ms_longest_first"):
+                               [round(float(p0[2]), 3), round(float(p0[3]), 3)]}
         # one context-parallel rank's share at its real shape: the long-context workload over 8 ranks,
         # each rank's contiguous 16384 query rows against all keys
         del wl

@@ -30,6 +30,10 @@
  *  - bounds is int32 [B, Hm, ceil(N / fm_kblock()), 8] as written by fm_tile_bounds for the same
  *    vectors. It may be NULL only when all four vectors are NULL. Bounds that do not belong to the
  *    vectors give wrong results but never out-of-range memory accesses.
+ *  - sched is NULL or an int32 schedule written by fm_tile_schedule for the same bounds, sizes, q_off
+ *    and causal flag. It changes only the order in which work units are dispatched, never a result
+ *    (every unit is independent and accumulates on chip). A schedule array of the right size whose
+ *    content does not belong to the problem gives wrong results but never out-of-range accesses.
  *  - Outputs must not alias inputs or each other.
  */
 #ifndef FM_H
@@ -76,6 +80,23 @@ size_t fm_bounds_elems(int B, int Hm, int N);
 fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute,
                          int B, int Hm, int N, int32_t* bounds, hipStream_t stream);
 
+/* Longest-first dispatch schedule (the single-GPU form of the sparsity-aware load balancing that the
+ * FlashMask-3 summary, readmex.ai, applies to masked attention across workers). The kernels' work units
+ * are query units of 128 rows (forward, dq) and key units of 128 columns (dk, dv); the work of a unit is
+ * the number of tiles on its row of the tile grid (64-column key tiles) or its column (64-row query
+ * tiles) that the tile classification does not mark fully masked, with rows q_off + i. For each
+ * (b, hm) row of the mask, with nq = ceil(Nq / 128) and nk = ceil(Nk / 128), sched holds
+ *   [0, nq)              the query units in decreasing order of work (equal work: latest unit first)
+ *   [nq, nq + nk)        the key units in decreasing order of work (equal work: earliest unit first)
+ *   [nq + nk, 2nq + nk)  the work of each query unit, then [2nq + nk, 2(nq + nk)) that of each key unit.
+ * Workgroups are handed to the hardware in that order, which is the longest-processing-time-first list
+ * rule; equal work keeps the order used without a schedule. bounds as for fm_fwd (NULL when there are no
+ * vectors); sched is a caller-owned device array of fm_schedule_elems(B, Hm, Nq, Nk) int32.
+ * Errors: FM_ERR_INVALID (sched NULL, sizes out of range), FM_ERR_LAUNCH. */
+size_t fm_schedule_elems(int B, int Hm, int Nq, int Nk);
+fm_status fm_tile_schedule(const int32_t* bounds, int B, int Hm, int Nq, int Nk, int q_off, int causal,
+                           int32_t* sched, hipStream_t stream);
+
 /* Forward pass (FlashMask abstract: exact attention with mask-driven skipping; FlashAttention-3
  * abstract, fugumt.com 2407.08608: tiled online softmax).
  *   out[b,h,i,:] = sum_j P_ij v[b,h,j,:],  P_ij = exp(S_ij - lse_i) on unmasked (i, j), 0 elsewhere,
@@ -87,7 +108,8 @@ fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* 
  * Errors: FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_LAUNCH. */
 fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
                  const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
-                 const int32_t* bounds, int causal, float scale, void* out, float* lse, hipStream_t stream);
+                 const int32_t* bounds, const int32_t* sched, int causal, float scale, void* out, float* lse,
+                 hipStream_t stream);
 
 /* Device workspace fm_bwd needs: the float32 [B, H, N] row term D_i = sum_k dout_ik out_ik, rounded up
  * to 256 bytes. 0 on bad sizes. */
@@ -104,8 +126,8 @@ size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d);
 fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, fm_dtype dtype, int B, int H, int N, int d,
                  const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
-                 const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+                 const int32_t* bounds, const int32_t* sched, int causal, float scale, void* dq, void* dk,
+                 void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One block of query rows against all keys: the unit of work of one rank under context parallelism,
  * whose mask localisation is a zero-communication clip-shift-max on the boundary vectors that keeps the
@@ -117,17 +139,18 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
  *   vectors: int32 [B, Hm, Nk] (values are global query rows); bounds from fm_tile_bounds(..., Nk, ...).
  * out, lse and dq are exactly those rows of the whole problem; dk and dv are the contributions of these
  * rows only (summing them over a partition of the rows gives the whole dk, dv). The workspace is
- * fm_bwd_workspace_bytes(dtype, B, H, Nq, d). fm_fwd / fm_bwd are the case Nq = Nk = N, q_off = 0.
+ * fm_bwd_workspace_bytes(dtype, B, H, Nq, d); a schedule comes from fm_tile_schedule(..., Nq, Nk, q_off, ...).
+ * fm_fwd / fm_bwd are the case Nq = Nk = N, q_off = 0.
  * Errors as fm_fwd / fm_bwd; also FM_ERR_INVALID for q_off < 0 or q_off + Nq > FM_MAX_N. */
 fm_status fm_fwd_rows(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int Nq, int Nk,
                       int q_off, int d, const int32_t* lts, const int32_t* lte, const int32_t* uts,
-                      const int32_t* ute, int Hm, const int32_t* bounds, int causal, float scale, void* out,
-                      float* lse, hipStream_t stream);
+                      const int32_t* ute, int Hm, const int32_t* bounds, const int32_t* sched, int causal,
+                      float scale, void* out, float* lse, hipStream_t stream);
 fm_status fm_bwd_rows(const void* q, const void* k, const void* v, const void* out, const void* dout,
                       const float* lse, fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d,
                       const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
-                      const int32_t* bounds, int causal, float scale, void* dq, void* dk, void* dv, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+                      const int32_t* bounds, const int32_t* sched, int causal, float scale, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Key compaction for masks that drop whole key columns (per-head key dropping with compute reduced in
  * proportion to the keys kept: SCFA review, nubint.ai, "proposed method"). A column is dropped when it

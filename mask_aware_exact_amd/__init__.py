@@ -2,9 +2,9 @@
 
 Argument marshalling only: torch supplies device memory and the current stream, every step of the
 path runs in the HIP kernels behind the C ABI declared in include/fm.h. The entry points keep the C
-names: fm_tile_bounds, fm_fwd, fm_bwd, their row-block forms fm_fwd_rows and fm_bwd_rows, the
-key-compaction pair fm_compact_keys and fm_gather_rows
-(plus fm_tile_classes, a test hook). There is no fallback:
+names: fm_tile_bounds, fm_tile_schedule, fm_fwd, fm_bwd, their row-block forms fm_fwd_rows and
+fm_bwd_rows, the key-compaction pair fm_compact_keys and fm_gather_rows (plus fm_tile_classes, a test
+hook). There is no fallback:
 if libfm.so is missing or cannot be loaded, every call raises.
 """
 from __future__ import annotations
@@ -21,7 +21,8 @@ FM_OK, FM_ERR_INVALID, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_LAUNCH = 0, 
 FM_BF16, FM_F32 = 0, 1
 NONE, PARTIAL, FULL = 0, 1, 2
 
-EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_fwd",
+EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_schedule_elems",
+            "fm_tile_schedule", "fm_fwd",
             "fm_bwd_workspace_bytes", "fm_bwd", "fm_fwd_rows", "fm_bwd_rows", "fm_tile_classes",
             "fm_compact_keys", "fm_gather_rows", "fm_status_str")
 
@@ -53,17 +54,22 @@ def load_library(path: str = LIB_PATH):
     lib.fm_tile_bounds.restype = I
     lib.fm_tile_bounds.argtypes = [P, P, P, P, I, I, I, P, P]
     lib.fm_fwd.restype = I
-    lib.fm_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P]
+    lib.fm_schedule_elems.restype = S
+    lib.fm_schedule_elems.argtypes = [I, I, I, I]
+    lib.fm_tile_schedule.restype = I
+    lib.fm_tile_schedule.argtypes = [P, I, I, I, I, I, I, P, P]
+    lib.fm_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P]
     lib.fm_bwd_workspace_bytes.restype = S
     lib.fm_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fm_bwd.restype = I
-    lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P, P, S, P]
+    lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P, S, P]
     lib.fm_tile_classes.restype = I
     lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
     lib.fm_fwd_rows.restype = I
-    lib.fm_fwd_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P]
+    lib.fm_fwd_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P]
     lib.fm_bwd_rows.restype = I
-    lib.fm_bwd_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, I, F, P, P, P, P, S, P]
+    lib.fm_bwd_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P, S,
+                                P]
     lib.fm_compact_keys.restype = I
     lib.fm_compact_keys.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P]
     lib.fm_gather_rows.restype = I
@@ -147,32 +153,57 @@ def fm_tile_bounds(lts, lte, uts, ute, B: int, Hm: int, N: int, bounds=None, str
     return bounds.view(B, Hm, -1, 8)
 
 
+def fm_schedule_elems(B: int, Hm: int, Nq: int, Nk: int) -> int:
+    return load_library().fm_schedule_elems(B, Hm, Nq, Nk)
+
+
+def fm_tile_schedule(bounds, B: int, Hm: int, Nq: int, Nk: int, causal: bool, q_off: int = 0, sched=None,
+                     device=None, stream=None):
+    """int32 [B, Hm, 2 (nq + nk)] longest-first dispatch schedule (nq = ceil(Nq/128), nk = ceil(Nk/128)):
+    query-unit order, key-unit order, then the work of each query unit and of each key unit."""
+    lib = load_library()
+    _need_cuda(bounds)
+    n = fm_schedule_elems(B, Hm, Nq, Nk)
+    if sched is None:
+        dev = bounds.device if bounds is not None else (device or torch.device("cuda"))
+        sched = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    _check(lib.fm_tile_schedule(_ptr(bounds), B, Hm, Nq, Nk, int(q_off), int(bool(causal)), _ptr(sched),
+                                _stream(stream)), "fm_tile_schedule")
+    return sched[:n].view(B, Hm, -1)
+
+
+def split_schedule(sched, Nq: int, Nk: int):
+    """(query order, key order, query work, key work) views of a [B, Hm, 2 (nq + nk)] schedule."""
+    nq, nk = -(-Nq // 128), -(-Nk // 128)
+    return sched[..., :nq], sched[..., nq:nq + nk], sched[..., nq + nk:2 * nq + nk], sched[..., 2 * nq + nk:]
+
+
 def fm_fwd(q, k, v, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False, scale=None,
-           out=None, lse=None, stream=None):
+           out=None, lse=None, stream=None, sched=None):
     """(out, lse) for q, k, v of shape [B, H, N, d]; vectors int32 [B, Hm, N] or None."""
     lib = load_library()
     B, H, N, d = q.shape
     vecs = [_vec(x) for x in (lts, lte, uts, ute)]
     Hm = next((x.shape[1] for x in vecs if x is not None), 1)
-    _need_cuda(q, k, v, bounds, *vecs)
+    _need_cuda(q, k, v, bounds, sched, *vecs)
     if scale is None:
         scale = d ** -0.5
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(lib.fm_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, N, d, *[_ptr(x) for x in vecs], Hm,
-                      _ptr(bounds), int(bool(causal)), float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+                      _ptr(bounds), _ptr(sched), int(bool(causal)), float(scale), _ptr(out), _ptr(lse), _stream(stream)),
            "fm_fwd")
     return out, lse
 
 
 def fm_bwd(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False,
-           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+           scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, sched=None):
     """(dq, dk, dv): gradients of sum(out * dout)."""
     lib = load_library()
     B, H, N, d = q.shape
     vecs = [_vec(x) for x in (lts, lte, uts, ute)]
     Hm = next((x.shape[1] for x in vecs if x is not None), 1)
-    _need_cuda(q, k, v, out, dout, lse, bounds, *vecs)
+    _need_cuda(q, k, v, out, dout, lse, bounds, sched, *vecs)
     if scale is None:
         scale = d ** -0.5
     dq = torch.empty_like(q) if dq is None else dq
@@ -182,7 +213,7 @@ def fm_bwd(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, boun
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.fm_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N, d,
-                      *[_ptr(x) for x in vecs], Hm, _ptr(bounds), int(bool(causal)), float(scale), _ptr(dq),
+                      *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), int(bool(causal)), float(scale), _ptr(dq),
                       _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)), "fm_bwd")
     return dq, dk, dv
 
@@ -232,7 +263,7 @@ def fm_gather_rows(x, idx, y=None, stream=None):
 
 
 def fm_fwd_rows(q, k, v, q_off: int, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False,
-                scale=None, out=None, lse=None, stream=None):
+                scale=None, out=None, lse=None, stream=None, sched=None):
     """(out, lse) for the query rows q_off .. q_off + Nq - 1 (q: [B, H, Nq, d]) against all keys
     (k, v: [B, H, Nk, d]); vectors int32 [B, Hm, Nk] in global row coordinates."""
     lib = load_library()
@@ -240,26 +271,27 @@ def fm_fwd_rows(q, k, v, q_off: int, lts=None, lte=None, uts=None, ute=None, bou
     Nk = k.shape[2]
     vecs = [_vec(x) for x in (lts, lte, uts, ute)]
     Hm = next((x.shape[1] for x in vecs if x is not None), 1)
-    _need_cuda(q, k, v, bounds, *vecs)
+    _need_cuda(q, k, v, bounds, sched, *vecs)
     if scale is None:
         scale = d ** -0.5
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(lib.fm_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, Nq, Nk, int(q_off), d,
-                           *[_ptr(x) for x in vecs], Hm, _ptr(bounds), int(bool(causal)), float(scale), _ptr(out),
+                           *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), int(bool(causal)), float(scale),
+                           _ptr(out),
                            _ptr(lse), _stream(stream)), "fm_fwd_rows")
     return out, lse
 
 
 def fm_bwd_rows(q, k, v, out, dout, lse, q_off: int, lts=None, lte=None, uts=None, ute=None, bounds=None,
-                causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+                causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, sched=None):
     """(dq, dk, dv) of the row block: dq for its rows, dk / dv the contributions of its rows."""
     lib = load_library()
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     vecs = [_vec(x) for x in (lts, lte, uts, ute)]
     Hm = next((x.shape[1] for x in vecs if x is not None), 1)
-    _need_cuda(q, k, v, out, dout, lse, bounds, *vecs)
+    _need_cuda(q, k, v, out, dout, lse, bounds, sched, *vecs)
     if scale is None:
         scale = d ** -0.5
     dq = torch.empty_like(q) if dq is None else dq
@@ -269,7 +301,8 @@ def fm_bwd_rows(q, k, v, out, dout, lse, q_off: int, lts=None, lte=None, uts=Non
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.fm_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, Nq,
-                           Nk, int(q_off), d, *[_ptr(x) for x in vecs], Hm, _ptr(bounds), int(bool(causal)),
+                           Nk, int(q_off), d, *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched),
+                           int(bool(causal)),
                            float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                            _stream(stream)), "fm_bwd_rows")
     return dq, dk, dv

@@ -36,6 +36,9 @@ struct BwdArgs {
   int Nq, Nk;  // query rows and keys per head
   int q_off;   // global index of query row 0: the mask and the causal rule see rows q_off + i
   int nkb;  // bounds entries per (b, hm) row
+  const int* sched;  // longest-first unit order (query units at 0, key units at sched_nq) or null
+  int sched_stride;  // int32 per (b, hm) row of sched
+  int sched_nq;      // query units of 128 rows
   int causal;
   float scale;
   float scale_log2;
@@ -78,10 +81,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int BH = a.B * a.H;
   const int nq = (a.Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
-  const int qt = nq - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) query tiles first
+  const int rank = (int)(blockIdx.x / BH);
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
+  // without a schedule the heaviest (latest) query tiles go first
+  static_assert(BR == SCHED_UNIT, "query units of the schedule are dq tiles");
+  const int qt = scheduled_unit(a.sched, a.sched_stride, (size_t)b * a.Hm + hm, 0, rank, nq, nq - 1 - rank);
+  if (qt < 0) return;
   const int Nq = a.Nq, N = a.Nk;  // N: keys
   const int r0 = qt * BR;
   const int r1 = min(Nq, r0 + BR);
@@ -340,10 +347,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  const int kt = (int)(blockIdx.x / BH);  // early key tiles carry the most causal work: dispatch them first
+  const int rank = (int)(blockIdx.x / BH);
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
+  // without a schedule early key tiles, which carry the most causal work, go first
+  static_assert(BC == SCHED_UNIT, "key units of the schedule are dk/dv tiles");
+  const int kt = scheduled_unit(a.sched, a.sched_stride, (size_t)b * a.Hm + hm, a.sched_nq, rank,
+                                (a.Nk + BC - 1) / BC, rank);
+  if (kt < 0) return;
   const int N = a.Nk, Nq = a.Nq, qoff = a.q_off;  // N: keys
   const int c0 = kt * BC;
   const int c1 = min(N, c0 + BC);
@@ -596,10 +608,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  const int kt = (int)(blockIdx.x / BH);
+  const int rank = (int)(blockIdx.x / BH);
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
+  // without a schedule early key tiles, which carry the most causal work, go first
+  static_assert(BC == SCHED_UNIT, "key units of the schedule are dk/dv tiles");
+  const int kt = scheduled_unit(a.sched, a.sched_stride, (size_t)b * a.Hm + hm, a.sched_nq, rank,
+                                (a.Nk + BC - 1) / BC, rank);
+  if (kt < 0) return;
   const int N = a.Nk, Nq = a.Nq, qoff = a.q_off;  // N: keys
   const int c0 = kt * BC;
   const int c1 = min(N, c0 + BC);
@@ -719,7 +736,8 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
 hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
                       const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
-                      int Nk, int q_off, int Hm, int causal, float scale, hipStream_t stream) {
+                      int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
+                      hipStream_t stream) {
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.dd = dd;
   a.dq = dq; a.dk = dk; a.dv = dv;
@@ -727,6 +745,9 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
   a.B = B; a.H = H; a.Hm = Hm;
   a.Nq = Nq; a.Nk = Nk; a.q_off = q_off;
   a.nkb = (Nk + KBLOCK - 1) / KBLOCK;
+  a.sched = sched;
+  a.sched_nq = (Nq + SCHED_UNIT - 1) / SCHED_UNIT;
+  a.sched_stride = 2 * (a.sched_nq + (Nk + SCHED_UNIT - 1) / SCHED_UNIT);
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * LOG2E;

@@ -75,6 +75,21 @@ __device__ inline TileBounds merged_bounds(const int* __restrict__ brow, int kt0
   return r;
 }
 
+// Rows of a query work unit (forward, dq) and columns of a key work unit (dk, dv): the granule of the
+// dispatch schedule.
+constexpr int SCHED_UNIT = 128;
+
+// Work unit of the workgroup at dispatch position `rank`: entry rank of the (b, hm) mask row `mrow` of a
+// longest-first schedule (order at offset `off` of a row of `stride` int32), or `fallback` without a
+// schedule. A scheduled value outside [0, n) gives -1: the workgroup does nothing, so a schedule that does
+// not belong to the problem can give wrong results but never out-of-range accesses.
+__device__ __forceinline__ int scheduled_unit(const int* __restrict__ sched, int stride, size_t mrow, int off,
+                                              int rank, int n, int fallback) {
+  if (sched == nullptr) return fallback;
+  const int u = sched[mrow * stride + off + rank];
+  return (u >= 0 && u < n) ? u : -1;
+}
+
 // Live-tile window over 64 consecutive tiles: bit t of `live` / `partial` describes tile base + t.
 // One wave-wide ballot classifies 64 tiles at once; every wave of a workgroup computes the same window.
 struct TileWindow {

@@ -43,6 +43,8 @@ struct FwdArgs {
   int q_off;   // global index of query row 0: the mask and the causal rule see rows q_off + i
   int nq;   // query tiles per head
   int nkb;  // bounds entries per (b, hm) row
+  const int* sched;  // longest-first unit order (query units at offset 0) or null
+  int sched_stride;  // int32 per (b, hm) row of sched
   int causal;
   float scale_log2;  // scale * log2(e)
 };
@@ -88,10 +90,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  const int qt = a.nq - 1 - (int)(blockIdx.x / BH);
+  const int rank = (int)(blockIdx.x / BH);
   const int b = bh / a.H;
   const int h = bh % a.H;
   const int hm = a.Hm > 1 ? h : 0;
+  static_assert(BR == SCHED_UNIT, "query units of the schedule are forward tiles");
+  const int qt = scheduled_unit(a.sched, a.sched_stride, (size_t)b * a.Hm + hm, 0, rank, a.nq, a.nq - 1 - rank);
+  if (qt < 0) return;
   const int Nq = a.Nq, N = a.Nk;  // N: keys
   const int r0 = qt * BR;
   const int r1 = min(Nq, r0 + BR);
@@ -330,7 +335,8 @@ int fwd_qblock() { return 128; }
 
 hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
                       const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
-                      int Nq, int Nk, int q_off, int Hm, int causal, float scale, hipStream_t stream) {
+                      int Nq, int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
+                      hipStream_t stream) {
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
   a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
@@ -338,6 +344,8 @@ hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const v
   a.Nq = Nq; a.Nk = Nk; a.q_off = q_off;
   a.nq = (Nq + 127) / 128;
   a.nkb = (Nk + KBLOCK - 1) / KBLOCK;
+  a.sched = sched;
+  a.sched_stride = 2 * (a.nq + (Nk + SCHED_UNIT - 1) / SCHED_UNIT);
   a.causal = causal;
   a.scale_log2 = scale * LOG2E;
   if (bf16_in) return d == 64 ? launch_fwd_t<bf16, 64>(a, stream) : launch_fwd_t<bf16, 128>(a, stream);

@@ -30,23 +30,36 @@ QSUB = 64    # query rows per tile of a key unit
 KSUB = 64    # key columns per tile of a query unit
 
 
+def query_unit_work(b64, causal: bool, Nq: int, Nk: int, q_off: int, qt: int) -> int:
+    """Key tiles of 64 columns (bounds b64 [ceil(Nk/64), 8]) not FULL for query unit qt."""
+    r0, r1 = q_off + qt * QUNIT, q_off + min(Nq, (qt + 1) * QUNIT)
+    n = 0
+    for kt in range(b64.shape[0]):
+        c0, c1 = kt * KSUB, min(Nk, (kt + 1) * KSUB)
+        n += OT.classify(r0, r1, c0, c1, b64[kt], causal) != OT.FULL
+    return n
+
+
+def key_unit_work(b128, causal: bool, Nq: int, Nk: int, q_off: int, kt: int) -> int:
+    """Query tiles of 64 rows not FULL for key unit kt (bounds b128 [ceil(Nk/128), 8] over 128 columns)."""
+    c0, c1 = kt * KUNIT, min(Nk, (kt + 1) * KUNIT)
+    n = 0
+    for qt in range(-(-Nq // QSUB)):
+        r0, r1 = q_off + qt * QSUB, q_off + min(Nq, (qt + 1) * QSUB)
+        n += OT.classify(r0, r1, c0, c1, b128[kt], causal) != OT.FULL
+    return n
+
+
+def unit_bounds(lts, lte, uts, ute, Nk: int):
+    """(b64, b128): per-tile min/max of the vectors over 64 and over 128 key columns."""
+    return (OT.tile_bounds_slice(lts, lte, uts, ute, Nk, KSUB), OT.tile_bounds_slice(lts, lte, uts, ute, Nk, KUNIT))
+
+
 def unit_costs_slice(lts, lte, uts, ute, causal: bool, Nq: int, Nk: int, q_off: int = 0):
     """(qcost [ceil(Nq/128)], kcost [ceil(Nk/128)]) for one (b, hm) slice of the [Nk] vectors."""
-    nq, nk = -(-Nq // QUNIT), -(-Nk // KUNIT)
-    b64 = OT.tile_bounds_slice(lts, lte, uts, ute, Nk, KSUB)
-    b128 = OT.tile_bounds_slice(lts, lte, uts, ute, Nk, KUNIT)
-    qcost = np.zeros(nq, np.int64)
-    for qt in range(nq):
-        r0, r1 = q_off + qt * QUNIT, q_off + min(Nq, (qt + 1) * QUNIT)
-        for kt in range(b64.shape[0]):
-            c0, c1 = kt * KSUB, min(Nk, (kt + 1) * KSUB)
-            qcost[qt] += OT.classify(r0, r1, c0, c1, b64[kt], causal) != OT.FULL
-    kcost = np.zeros(nk, np.int64)
-    for kt in range(nk):
-        c0, c1 = kt * KUNIT, min(Nk, (kt + 1) * KUNIT)
-        for qt in range(-(-Nq // QSUB)):
-            r0, r1 = q_off + qt * QSUB, q_off + min(Nq, (qt + 1) * QSUB)
-            kcost[kt] += OT.classify(r0, r1, c0, c1, b128[kt], causal) != OT.FULL
+    b64, b128 = unit_bounds(lts, lte, uts, ute, Nk)
+    qcost = np.array([query_unit_work(b64, causal, Nq, Nk, q_off, qt) for qt in range(-(-Nq // QUNIT))], np.int64)
+    kcost = np.array([key_unit_work(b128, causal, Nq, Nk, q_off, kt) for kt in range(-(-Nk // KUNIT))], np.int64)
     return qcost, kcost
 
 

@@ -52,15 +52,18 @@ def device_vectors(spec: W.MaskSpec, dev="cuda"):
     return [None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in spec.vectors()]
 
 
-def run_gpu(case: Case, fm, dev="cuda"):
-    """fm_tile_bounds -> fm_fwd -> fm_bwd through the C ABI; returns CPU tensors."""
+def run_gpu(case: Case, fm, dev="cuda", sched=False):
+    """fm_tile_bounds -> (fm_tile_schedule if sched) -> fm_fwd -> fm_bwd through the C ABI; returns CPU
+    tensors."""
     q, k, v, do = (t.to(dev) for t in (case.q, case.k, case.v, case.do))
     vecs = device_vectors(case.spec, dev)
     bounds = None
     if any(x is not None for x in vecs):
         bounds = fm.fm_tile_bounds(*vecs, case.B, case.spec.Hm, case.N)
-    out, lse = fm.fm_fwd(q, k, v, *vecs, bounds=bounds, causal=case.spec.causal, scale=case.scale)
-    dq, dk, dv = fm.fm_bwd(q, k, v, out, do, lse, *vecs, bounds=bounds, causal=case.spec.causal,
+    s = fm.fm_tile_schedule(bounds, case.B, case.spec.Hm, case.N, case.N, case.spec.causal,
+                            device=torch.device(dev)) if sched else None
+    out, lse = fm.fm_fwd(q, k, v, *vecs, bounds=bounds, sched=s, causal=case.spec.causal, scale=case.scale)
+    dq, dk, dv = fm.fm_bwd(q, k, v, out, do, lse, *vecs, bounds=bounds, sched=s, causal=case.spec.causal,
                            scale=case.scale)
     torch.cuda.synchronize()
     res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "bounds": bounds}

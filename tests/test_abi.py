@@ -57,11 +57,11 @@ B_ = P(0x200000)
 
 def _fwd(lib, **kw):
     args = dict(q=A, k=A, v=A, dtype=fm.FM_BF16, B=1, H=2, N=100, d=64, lts=None, lte=None, uts=None,
-                ute=None, Hm=1, bounds=None, causal=1, scale=0.125, out=B_, lse=B_)
+                ute=None, Hm=1, bounds=None, sched=None, causal=1, scale=0.125, out=B_, lse=B_)
     args.update(kw)
     return lib.fm_fwd(args["q"], args["k"], args["v"], args["dtype"], args["B"], args["H"], args["N"],
                       args["d"], args["lts"], args["lte"], args["uts"], args["ute"], args["Hm"], args["bounds"],
-                      args["causal"], args["scale"], args["out"], args["lse"], None)
+                      args["sched"], args["causal"], args["scale"], args["out"], args["lse"], None)
 
 
 def test_fwd_validation(lib):
@@ -87,12 +87,13 @@ def test_fwd_validation(lib):
 
 def _bwd(lib, **kw):
     args = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, dtype=fm.FM_BF16, B=1, H=2, N=100, d=64, lts=None,
-                lte=None, uts=None, ute=None, Hm=1, bounds=None, causal=1, scale=0.125, dq=B_, dk=B_, dv=B_,
+                lte=None, uts=None, ute=None, Hm=1, bounds=None, sched=None, causal=1, scale=0.125, dq=B_, dk=B_,
+                dv=B_,
                 ws=P(0x300000), ws_bytes=1 << 30)
     args.update(kw)
     return lib.fm_bwd(args["q"], args["k"], args["v"], args["out"], args["dout"], args["lse"], args["dtype"],
                       args["B"], args["H"], args["N"], args["d"], args["lts"], args["lte"], args["uts"],
-                      args["ute"], args["Hm"], args["bounds"], args["causal"], args["scale"], args["dq"],
+                      args["ute"], args["Hm"], args["bounds"], args["sched"], args["causal"], args["scale"], args["dq"],
                       args["dk"], args["dv"], args["ws"], args["ws_bytes"], None)
 
 
@@ -163,10 +164,11 @@ def test_gather_validation(lib):
 
 
 def test_rows_validation(lib):
-    # (q, k, v, dtype, B, H, Nq, Nk, q_off, d, lts, lte, uts, ute, Hm, bounds, causal, scale, out, lse, stream)
+    # (q, k, v, dtype, B, H, Nq, Nk, q_off, d, lts, lte, uts, ute, Hm, bounds, sched, causal, scale, out, lse,
+    #  stream)
     def fwd_rows(Nq=100, Nk=100, q_off=0):
-        return lib.fm_fwd_rows(A, A, A, fm.FM_BF16, 1, 2, Nq, Nk, q_off, 64, None, None, None, None, 1, None, 1,
-                               0.125, B_, B_, None)
+        return lib.fm_fwd_rows(A, A, A, fm.FM_BF16, 1, 2, Nq, Nk, q_off, 64, None, None, None, None, 1, None, None,
+                               1, 0.125, B_, B_, None)
     assert fwd_rows(q_off=-1) == fm.FM_ERR_INVALID
     assert fwd_rows(Nk=0) == fm.FM_ERR_INVALID
     assert fwd_rows(Nq=0) == fm.FM_ERR_INVALID
@@ -175,6 +177,18 @@ def test_rows_validation(lib):
 
     def bwd_rows(q_off=0, wsb=ws):
         return lib.fm_bwd_rows(A, A, A, A, A, A, fm.FM_BF16, 1, 2, 100, 100, q_off, 64, None, None, None, None, 1,
-                               None, 1, 0.125, B_, B_, B_, A, wsb, None)
+                               None, None, 1, 0.125, B_, B_, B_, A, wsb, None)
     assert bwd_rows(q_off=-3) == fm.FM_ERR_INVALID
     assert bwd_rows(wsb=ws - 256) == fm.FM_ERR_WORKSPACE
+
+
+def test_schedule_validation(lib):
+    assert lib.fm_schedule_elems(1, 1, 1, 1) == 4
+    assert lib.fm_schedule_elems(2, 3, 300, 129) == 2 * 3 * 2 * (3 + 2)
+    assert lib.fm_schedule_elems(0, 1, 10, 10) == 0 and lib.fm_schedule_elems(1, 1, (1 << 24) + 1, 10) == 0
+    # (bounds, B, Hm, Nq, Nk, q_off, causal, sched, stream)
+    assert lib.fm_tile_schedule(A, 1, 1, 100, 100, 0, 1, None, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_schedule(A, 0, 1, 100, 100, 0, 1, B_, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_schedule(A, 1, 1, 100, 0, 0, 1, B_, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_schedule(A, 1, 1, 100, 100, -1, 1, B_, None) == fm.FM_ERR_INVALID
+    assert lib.fm_tile_schedule(A, 1, 1, 100, 100, (1 << 24) - 50, 1, B_, None) == fm.FM_ERR_INVALID
