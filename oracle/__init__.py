@@ -15,5 +15,6 @@ Modules:
   attention fp64 forward/backward (row-blocked), brute force for tiny cases, one-row/one-column probes
   compact   removal of the key columns masked for every row, and the compacted problem's mask
   schedule  longest-first order of the work units by their count of tiles that are not fully masked
+  hashing   LSH buckets, reordering by bucket with the reordered problem's mask, hash-bucket attention
 """
-from . import masks, tiles, attention, compact, schedule  # noqa: F401
+from . import masks, tiles, attention, compact, schedule, hashing  # noqa: F401
