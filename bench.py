@@ -115,13 +115,13 @@ def unmasked_pairs(spec: W.MaskSpec, H: int, rows=None) -> int:
 
 
 class Workload:
-    def __init__(self, name: str, device):
+    def __init__(self, name: str, device, cfg_mask=None):
         import torch
-        cfg_idx, mask = WORKLOADS[name]
+        cfg_idx, mask = WORKLOADS[name] if cfg_mask is None else cfg_mask
         cfg = W.CONFIGS[cfg_idx]
         self.name, self.cfg, self.mask = name, cfg, mask
         self.B, self.H, self.N, self.d = cfg.B, cfg.H, cfg.N, cfg.d
-        mi = cfg.masks.index(mask)
+        mi = cfg.masks.index(mask) if mask in cfg.masks else 0
         self.spec = W.make_mask(cfg.index, mask, cfg.B, cfg.H, cfg.N, mi)
         self.mask_index = mi
         q, k, v, do = W.make_tensors(cfg.index, mi, cfg.B, cfg.H, cfg.N, cfg.d)
@@ -256,6 +256,72 @@ def time_rows(fm, wl: Workload, a: int, b: int, steps: int, warmup: int):
         step()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+class HashWorkload:
+    """Hash-bucket attention at a configuration's shape: seeded Q, K, V, dO and one random rotation per
+    head; the buckets come from the library's own hash inside the timed step."""
+
+    def __init__(self, name: str, device):
+        import torch
+        cfg_idx, nb = W.HASH_WORKLOADS[name]
+        cfg = W.CONFIGS[cfg_idx]
+        self.name, self.cfg, self.nb = name, cfg, nb
+        self.B, self.H, self.N, self.d = cfg.B, cfg.H, cfg.N, cfg.d
+        host = W.make_tensors(cfg_idx, W.HASH_MASK_INDEX, cfg.B, cfg.H, cfg.N, cfg.d)
+        to = lambda x: torch.from_numpy(x).to(device=device).to(torch.bfloat16)  # noqa: E731
+        self.q, self.k, self.v, self.do = (to(x) for x in host)
+        del host
+        self.rot = torch.from_numpy(W.make_rotation(cfg_idx, W.HASH_MASK_INDEX, cfg.H, cfg.d, nb)).to(device)
+        self.scale = 1.0 / math.sqrt(self.d)
+
+
+def time_hash_workload(fm, wl: HashWorkload, steps: int, warmup: int):
+    """One step: fm_lsh_buckets of Q and K, fm_bucket_sort, fm_gather_rows of Q, K, V, dO into bucket
+    order, fm_tile_bounds, fm_fwd and fm_bwd (no causal flag), fm_gather_rows of out, dq, dk, dv back.
+    All of it is timed. U is counted from the reordered problem's vectors after the warmup."""
+    import torch
+    B, H, N = wl.B, wl.H, wl.N
+    qs, ks, vs, dos = (torch.empty_like(x) for x in (wl.q, wl.k, wl.v, wl.do))
+    outs = torch.empty_like(wl.q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=wl.q.device)
+    dqs, dks, dvs = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
+    out, dq, dk, dv = (torch.empty_like(x) for x in (wl.q, wl.q, wl.k, wl.v))
+    ws = torch.empty(fm.fm_bwd_workspace_bytes(torch.bfloat16, B, H, N, wl.d), dtype=torch.uint8,
+                     device=wl.q.device)
+    bounds = torch.empty(fm.fm_bounds_elems(B, H, N), dtype=torch.int32, device=wl.q.device)
+    qb = torch.empty((B, H, N), dtype=torch.int32, device=wl.q.device)
+    kb = torch.empty_like(qb)
+
+    def step():
+        fm.fm_lsh_buckets(wl.q, wl.rot, wl.nb, out=qb)
+        fm.fm_lsh_buckets(wl.k, wl.rot, wl.nb, out=kb)
+        qidx, qpos, kidx, kpos, vecs = fm.fm_bucket_sort(qb, kb, wl.nb)
+        fm.fm_gather_rows(wl.q, qidx, y=qs)
+        fm.fm_gather_rows(wl.do, qidx, y=dos)
+        fm.fm_gather_rows(wl.k, kidx, y=ks)
+        fm.fm_gather_rows(wl.v, kidx, y=vs)
+        b = fm.fm_tile_bounds(*vecs, B, H, N, bounds=bounds)
+        fm.fm_fwd(qs, ks, vs, *vecs, bounds=b, causal=False, scale=wl.scale, out=outs, lse=lse)
+        fm.fm_bwd(qs, ks, vs, outs, dos, lse, *vecs, bounds=b, causal=False, scale=wl.scale, dq=dqs, dk=dks,
+                  dv=dvs, workspace=ws)
+        fm.fm_gather_rows(outs, qpos, y=out)
+        fm.fm_gather_rows(dqs, qpos, y=dq)
+        fm.fm_gather_rows(dks, kpos, y=dk)
+        fm.fm_gather_rows(dvs, kpos, y=dv)
+        return vecs
+
+    for _ in range(warmup):
+        vecs = step()
+    torch.cuda.synchronize()
+    lts, _, _, ute = vecs
+    U = int(torch.clamp(lts.long() - ute.long(), min=0).sum())
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ok = bool(torch.isfinite(out.float()).all() and torch.isfinite(dk.float()).all())
+    return (time.perf_counter() - t0) / steps, U, ok
 
 
 def cpu_baseline(wl: Workload, budget_heads: int, max_tokens: int):
@@ -405,6 +471,23 @@ def main():
         sweep["dpo_rm_causal_key_drop (key compaction)"] = {
             "TFLOP/s": round(wl.flop / (w3 * 1e3 / n * 1e-3) / 1e12, 2), "ms_per_step": round(w3 * 1e3 / n, 3),
             "U": int(wl.U), "compactable": ok3}
+        # hash-bucket attention, against plain causal attention at the same shape
+        for name in W.HASH_WORKLOADS:
+            del wl
+            torch.cuda.empty_cache()
+            hw = HashWorkload(name, dev)
+            n = max(3, args.steps // 4)
+            t, U, okh = time_hash_workload(fm, hw, n, 1)
+            cfg_i, hd = W.HASH_WORKLOADS[name][0], hw.d
+            del hw
+            torch.cuda.empty_cache()
+            wl = Workload(name + " (plain causal)", dev, cfg_mask=(cfg_i, "causal"))
+            wc, _, _ = time_workload(fm, wl, n, 1)
+            causal_ms = wc * 1e3 / n
+            sweep[name] = {"TFLOP/s": round(14.0 * hd * U / t / 1e12, 2), "ms_per_step": round(t * 1e3, 3),
+                           "U": U, "buckets": W.HASH_WORKLOADS[name][1], "finite": okh,
+                           "plain_causal_ms_per_step": round(causal_ms, 3),
+                           "speedup_vs_plain_causal": round(causal_ms / (t * 1e3), 2)}
         rec["sweep"] = sweep
     print(json.dumps(rec), flush=True)
 

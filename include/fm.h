@@ -181,6 +181,36 @@ fm_status fm_compact_keys(const int32_t* lts, const int32_t* lte, const int32_t*
 fm_status fm_gather_rows(const void* x, fm_dtype dtype, int B, int H, int N, int d, const int32_t* idx, int Hm,
                          void* y, hipStream_t stream);
 
+/* Hash-bucket sparse causal attention (SCFA review, nubint.ai, "proposed method" and Figure 3: exact
+ * attention restricted to hash buckets, computed after reordering queries and keys by bucket, which gives
+ * a non-triangular causal mask). Query i attends key j iff both have the same bucket and j <= i.
+ *
+ * fm_lsh_buckets: Reformer-style geometric hash of each row of x [B, H, N, d] (dtype, 16-byte aligned):
+ *   buckets[b, h, i] = the first index of the maximum of the nb values [x_i R_h, -x_i R_h], with the
+ *   rotation R_h = rot[h] (Hr = H) or rot[0] (Hr = 1), float32 [Hr, d, nb / 2] row-major, a random matrix
+ *   the caller draws. Dot products are float32 fused multiply-adds over d in increasing order, so rows
+ *   whose top two values differ by less than float32 rounding may get either bucket.
+ *   Errors: FM_ERR_INVALID (NULL, sizes, Hr not in {1, H}, nb odd or outside [2, 64], x misaligned),
+ *   FM_ERR_UNSUPPORTED (d, dtype), FM_ERR_LAUNCH.
+ *
+ * fm_bucket_sort: for query buckets qbucket and key buckets kbucket, int32 [B, H, N] (a value outside
+ *   [0, nb) marks a dropped token, which attends and is attended by nothing), sorts queries and keys of
+ *   each head stably by bucket, dropped tokens last, and writes int32 [B, H, N] arrays:
+ *     qidx[r]  original query at sorted row r;     qpos[i]  sorted row of query i (inverse of qidx);
+ *     kidx[c]  original key at sorted column c;    kpos[j]  sorted column of key j;
+ *     lts .. ute  the sorted problem's mask (Hm = H, causal = 0): for the key at column c, of bucket b at
+ *       position p, with bucket b's queries in rows [qs, qe): UT = [0, lo) where lo = qs + (bucket-b
+ *       queries at positions < p), LT = [qe, N); a dropped key has UT = [0, N). Empty spans canonical.
+ *   Running fm_fwd / fm_bwd (causal = 0) on Q, dO gathered by qidx and K, V gathered by kidx
+ *   (fm_gather_rows) with these vectors computes the hash attention; out and dq come back by gathering
+ *   with qpos, dk and dv with kpos; lse stays in sorted order (row qpos[i] holds query i's).
+ *   Errors: FM_ERR_INVALID (NULL, sizes, nb outside [1, 512]), FM_ERR_LAUNCH. */
+fm_status fm_lsh_buckets(const void* x, fm_dtype dtype, int B, int H, int N, int d, const float* rot, int Hr,
+                         int nb, int32_t* buckets, hipStream_t stream);
+fm_status fm_bucket_sort(const int32_t* qbucket, const int32_t* kbucket, int B, int H, int N, int nb, int32_t* qidx,
+                         int32_t* qpos, int32_t* kidx, int32_t* kpos, int32_t* lts, int32_t* lte, int32_t* uts,
+                         int32_t* ute, hipStream_t stream);
+
 /* Test hook: the tile classifier the kernels use, materialised. For each (b, hm, query tile of
  * qblock rows, key tile of kblock columns), clipped to N, writes classes[b][hm][qt][kt]:
  *   2 FULL    the causal triangle or one interval covers every (row, column) of the tile

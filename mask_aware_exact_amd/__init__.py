@@ -3,8 +3,8 @@
 Argument marshalling only: torch supplies device memory and the current stream, every step of the
 path runs in the HIP kernels behind the C ABI declared in include/fm.h. The entry points keep the C
 names: fm_tile_bounds, fm_tile_schedule, fm_fwd, fm_bwd, their row-block forms fm_fwd_rows and
-fm_bwd_rows, the key-compaction pair fm_compact_keys and fm_gather_rows (plus fm_tile_classes, a test
-hook). There is no fallback:
+fm_bwd_rows, the key-compaction pair fm_compact_keys and fm_gather_rows, the hash-bucket pair
+fm_lsh_buckets and fm_bucket_sort (plus fm_tile_classes, a test hook). There is no fallback:
 if libfm.so is missing or cannot be loaded, every call raises.
 """
 from __future__ import annotations
@@ -24,7 +24,7 @@ NONE, PARTIAL, FULL = 0, 1, 2
 EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_schedule_elems",
             "fm_tile_schedule", "fm_fwd",
             "fm_bwd_workspace_bytes", "fm_bwd", "fm_fwd_rows", "fm_bwd_rows", "fm_tile_classes",
-            "fm_compact_keys", "fm_gather_rows", "fm_status_str")
+            "fm_compact_keys", "fm_gather_rows", "fm_lsh_buckets", "fm_bucket_sort", "fm_status_str")
 
 
 class FmError(RuntimeError):
@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH):
     lib.fm_compact_keys.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P]
     lib.fm_gather_rows.restype = I
     lib.fm_gather_rows.argtypes = [P, I, I, I, I, I, P, I, P, P]
+    lib.fm_lsh_buckets.restype = I
+    lib.fm_lsh_buckets.argtypes = [P, I, I, I, I, I, P, I, I, P, P]
+    lib.fm_bucket_sort.restype = I
+    lib.fm_bucket_sort.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, P]
     lib.fm_status_str.restype = ctypes.c_char_p
     lib.fm_status_str.argtypes = [I]
     _lib = lib
@@ -306,3 +310,33 @@ def fm_bwd_rows(q, k, v, out, dout, lse, q_off: int, lts=None, lte=None, uts=Non
                            float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                            _stream(stream)), "fm_bwd_rows")
     return dq, dk, dv
+
+
+def fm_lsh_buckets(x, rot, nb: int, out=None, stream=None):
+    """int32 [B, H, N] bucket of each row of x [B, H, N, d]: argmax of [x R, -x R] for rot float32
+    [Hr, d, nb / 2] (Hr = 1 or H)."""
+    lib = load_library()
+    B, H, N, d = x.shape
+    _need_cuda(x, rot)
+    if rot.dtype != torch.float32:
+        raise TypeError("rot must be float32")
+    out = torch.empty((B, H, N), dtype=torch.int32, device=x.device) if out is None else out
+    _check(lib.fm_lsh_buckets(_ptr(x), _dtype_code(x), B, H, N, d, _ptr(rot), rot.shape[0], nb, _ptr(out),
+                              _stream(stream)), "fm_lsh_buckets")
+    return out
+
+
+def fm_bucket_sort(qbucket, kbucket, nb: int, stream=None):
+    """(qidx, qpos, kidx, kpos, vectors): stable reordering of queries and keys by bucket (int32 [B, H, N]
+    inputs; values outside [0, nb) are dropped tokens) and the sorted problem's four int32 [B, H, N] mask
+    vectors, to be run with causal = False and Hm = H."""
+    lib = load_library()
+    qbucket, kbucket = _vec(qbucket), _vec(kbucket)
+    _need_cuda(qbucket, kbucket)
+    B, H, N = qbucket.shape
+    new = lambda: torch.empty((B, H, N), dtype=torch.int32, device=qbucket.device)  # noqa: E731
+    qidx, qpos, kidx, kpos = new(), new(), new(), new()
+    vecs = [new() for _ in range(4)]
+    _check(lib.fm_bucket_sort(_ptr(qbucket), _ptr(kbucket), B, H, N, nb, _ptr(qidx), _ptr(qpos), _ptr(kidx),
+                              _ptr(kpos), *[_ptr(x) for x in vecs], _stream(stream)), "fm_bucket_sort")
+    return qidx, qpos, kidx, kpos, vecs

@@ -29,6 +29,12 @@ hipError_t launch_compact_keys(const int* lts, const int* lte, const int* uts, c
                                int* ute2, hipStream_t stream);
 hipError_t launch_gather_rows(const void* x, const int* idx, int B, int H, int Hm, int N, int row_bytes, void* y,
                               hipStream_t stream);
+int lsh_max_nb();
+int sort_max_nb();
+hipError_t launch_lsh_buckets(bool bf16_in, int d, const void* x, const float* rot, int B, int H, int N, int Hr,
+                              int nb, int* out, hipStream_t stream);
+hipError_t launch_bucket_sort(const int* qb, const int* kb, int rows, int N, int nb, int* qidx, int* qpos,
+                              int* kidx, int* kpos, int* lts, int* lte, int* uts, int* ute, hipStream_t stream);
 }  // namespace fm
 
 namespace {
@@ -182,6 +188,27 @@ fm_status fm_gather_rows(const void* x, fm_dtype dtype, int B, int H, int N, int
   if (!aligned16(x) || !aligned16(y)) return FM_ERR_INVALID;
   const int row_bytes = d * (dtype == FM_BF16 ? 2 : 4);
   return from_hip(fm::launch_gather_rows(x, idx, B, H, Hm, N, row_bytes, y, stream));
+}
+
+fm_status fm_lsh_buckets(const void* x, fm_dtype dtype, int B, int H, int N, int d, const float* rot, int Hr,
+                         int nb, int32_t* buckets, hipStream_t stream) {
+  if (x == nullptr || rot == nullptr || buckets == nullptr) return FM_ERR_INVALID;
+  const fm_status st = dtype_d_ok(dtype, d);
+  if (st != FM_OK) return st;
+  if (!sizes_ok(B, H, N) || (Hr != 1 && Hr != H)) return FM_ERR_INVALID;
+  if (nb < 2 || nb > fm::lsh_max_nb() || (nb & 1) != 0 || !aligned16(x)) return FM_ERR_INVALID;
+  return from_hip(fm::launch_lsh_buckets(dtype == FM_BF16, d, x, rot, B, H, N, Hr, nb, buckets, stream));
+}
+
+fm_status fm_bucket_sort(const int32_t* qbucket, const int32_t* kbucket, int B, int H, int N, int nb, int32_t* qidx,
+                         int32_t* qpos, int32_t* kidx, int32_t* kpos, int32_t* lts, int32_t* lte, int32_t* uts,
+                         int32_t* ute, hipStream_t stream) {
+  if (qbucket == nullptr || kbucket == nullptr || qidx == nullptr || qpos == nullptr || kidx == nullptr ||
+      kpos == nullptr || lts == nullptr || lte == nullptr || uts == nullptr || ute == nullptr)
+    return FM_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || nb < 1 || nb > fm::sort_max_nb()) return FM_ERR_INVALID;
+  return from_hip(fm::launch_bucket_sort(qbucket, kbucket, B * H, N, nb, qidx, qpos, kidx, kpos, lts, lte, uts, ute,
+                                         stream));
 }
 
 fm_status fm_tile_classes(const int32_t* bounds, int B, int Hm, int N, int causal, int qblock, uint8_t* classes,

@@ -112,3 +112,44 @@ def hash_attention(q, k, v, do, qb, kb, nb: int, scale: float):
 def unmasked_count(qb, kb, nb: int) -> int:
     """Number of (query, key) pairs of one head that attend each other."""
     return int((~hash_masked(qb, kb, nb)).sum())
+
+
+def _row_keys(gq, gk, nb, i):
+    """Keys attended by query i: same group (not dropped) and position <= i."""
+    if gq[i] >= nb:
+        return np.zeros(0, np.int64)
+    return np.flatnonzero((gk[:i + 1] == gq[i]))
+
+
+def hash_rows_probe(q, k, v, do, qb, kb, nb: int, scale: float, rows):
+    """out, lse, dq of selected query rows of one head (original order), each from its full row."""
+    gq, gk = _group(qb, nb), _group(kb, nb)
+    d = q.shape[1]
+    outs, lses, dqs = [], [], []
+    for i in np.asarray(rows, np.int64):
+        keys = _row_keys(gq, gk, nb, int(i))
+        if keys.size == 0:
+            outs.append(np.zeros(d)); lses.append(-np.inf); dqs.append(np.zeros(d))
+            continue
+        res = attend_rows(q[i:i + 1], k[keys], v[keys], do[i:i + 1], np.zeros((1, keys.size), bool), scale)
+        outs.append(res["out"][0]); lses.append(res["lse"][0]); dqs.append(res["dq"][0])
+    return np.array(outs), np.array(lses), np.array(dqs)
+
+
+def hash_cols_probe(q, k, v, do, qb, kb, nb: int, scale: float, cols):
+    """dk, dv of selected key columns of one head: every query attending one of them is evaluated over
+    its full row and its contributions to the selected columns are summed."""
+    gq, gk = _group(qb, nb), _group(kb, nb)
+    N, d = q.shape
+    cols = np.asarray(cols, np.int64)
+    dk, dv = np.zeros((cols.size, d)), np.zeros((cols.size, d))
+    for n, j in enumerate(cols):
+        if gk[j] >= nb:
+            continue
+        for i in np.flatnonzero(gq[j:] == gk[j]) + j:
+            keys = _row_keys(gq, gk, nb, int(i))
+            res = attend_rows(q[i:i + 1], k[keys], v[keys], do[i:i + 1], np.zeros((1, keys.size), bool), scale)
+            t = int(np.searchsorted(keys, j))
+            dk[n] += scale * res["dS"][0, t] * q[i]
+            dv[n] += res["P"][0, t] * do[i]
+    return dk, dv

@@ -119,3 +119,20 @@ def test_gradients_against_float64_autograd():
     assert np.allclose(out, o.detach().numpy(), atol=1e-12)
     for got, t in ((dq, tq), (dk, tk), (dv, tv)):
         assert np.allclose(got, t.grad.numpy(), atol=1e-11)
+
+
+def test_probes_match_the_whole_head():
+    rng = np.random.default_rng(8)
+    N, d, nb = 60, 8, 3
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    qb = rng.integers(-1, nb, size=N)
+    kb = rng.integers(0, nb + 1, size=N)
+    out, lse, dq, dk, dv = OH.hash_attention_head(q, k, v, do, qb, kb, nb, 0.4)
+    rows = np.arange(N)
+    po, pl, pdq = OH.hash_rows_probe(q, k, v, do, qb, kb, nb, 0.4, rows)
+    assert np.allclose(po, out, atol=1e-12) and np.allclose(pdq, dq, atol=1e-12)
+    assert np.array_equal(np.isfinite(pl), np.isfinite(lse))
+    fin = np.isfinite(lse)
+    assert np.allclose(pl[fin], lse[fin], atol=1e-12)
+    pdk, pdv = OH.hash_cols_probe(q, k, v, do, qb, kb, nb, 0.4, rows)
+    assert np.allclose(pdk, dk, atol=1e-12) and np.allclose(pdv, dv, atol=1e-12)

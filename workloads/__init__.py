@@ -24,6 +24,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 PURPOSE_MASK, PURPOSE_Q, PURPOSE_K, PURPOSE_V, PURPOSE_DO = 0, 1, 2, 3, 4
+PURPOSE_ROT, PURPOSE_BUCKET = 5, 6
 
 
 @dataclass
@@ -274,4 +275,36 @@ def make_tensors(cfg: int, mask_index: int, B: int, H: int, N: int, d: int):
     for purpose in (PURPOSE_Q, PURPOSE_K, PURPOSE_V, PURPOSE_DO):
         rng = rng_for(cfg, mask_index, purpose)
         out.append(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    return tuple(out)
+
+
+# ---------------------------------------------------------------- hash-bucket attention inputs
+# The hash needs a random matrix per head; it is drawn here and passed in, like Q, K, V and dO. The
+# hash-bucket workloads use the SFT shape (8192 tokens) with 8 and 16 buckets, the setting of the SCFA
+# review's hash-attention timings, and the long-context shape with 16 buckets.
+
+HASH_WORKLOADS = {
+    # name: (config index, buckets)
+    "sft_packing_hash_8": (2, 8),
+    "sft_packing_hash_16": (2, 16),
+    "long_context_hash_16": (4, 16),
+}
+HASH_MASK_INDEX = 100  # seed stream of the hash workloads, apart from the mask families'
+
+
+def make_rotation(cfg: int, mask_index: int, H: int, d: int, nb: int) -> np.ndarray:
+    """float32 N(0, 1) [H, d, nb / 2]: one random rotation per head for the bucket hash."""
+    return rng_for(cfg, mask_index, PURPOSE_ROT).standard_normal((H, d, nb // 2), dtype=np.float32)
+
+
+def make_buckets(cfg: int, mask_index: int, B: int, H: int, N: int, nb: int, drop: float = 0.0):
+    """int32 [B, H, N] query and key bucket ids, uniform in [0, nb), with a fraction `drop` of each set
+    to -1 (dropped token): inputs for the reordering and the attention independent of any hash."""
+    rng = rng_for(cfg, mask_index, PURPOSE_BUCKET)
+    out = []
+    for _ in range(2):
+        bk = rng.integers(0, nb, size=(B, H, N)).astype(np.int32)
+        if drop > 0:
+            bk[rng.random((B, H, N)) < drop] = -1
+        out.append(bk)
     return tuple(out)
