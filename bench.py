@@ -355,7 +355,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(W.HASH_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
@@ -378,6 +378,19 @@ def main():
     fm.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.workload in W.HASH_WORKLOADS:
+        hw = HashWorkload(args.workload, dev)
+        t, U, okh = time_hash_workload(fm, hw, args.steps, args.warmup)
+        tfl = 14.0 * hw.d * U / t / 1e12
+        print(json.dumps({
+            "metric": METRIC, "value": round(tfl, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": hw.name, "B": hw.B, "H": hw.H, "N": hw.N, "d": hw.d, "buckets": hw.nb,
+                       "unmasked_pairs": U, "flop_formula": "14*d*U"},
+            "pct_of_peak": round(100.0 * tfl / PEAK_BF16_TFLOPS, 2), "finite_outputs": okh}), flush=True)
+        return
 
     wl = Workload(args.workload, dev)
     use_sched = args.schedule

@@ -9,7 +9,7 @@
 // p). So the key's column is masked on UT = [0, lo_c) and LT = [qe_b, N), and the attention kernels run
 // unchanged (causal flag off).
 //   fm_lsh_buckets  bucket of each row: argmax of [x R, -x R] for a random R [d, nb/2] (Reformer-style
-//                   geometric hashing), float32 dot products.
+//                   geometric hashing), float32 dot products; HBM-bound (2 d bytes read per bf16 row).
 //   fm_bucket_sort  stable counting sort of queries and keys by bucket (out-of-range buckets form a
 //                   trailing dropped group that attends and is attended by nothing), the permutations
 //                   both ways, and the sorted problem's four vectors, in one sweep per head.
@@ -19,77 +19,140 @@ namespace fm {
 
 namespace {
 
-constexpr int LSH_T = 256;     // rows per workgroup, one per thread
+constexpr int LSH_T = 256;     // threads and rows per workgroup (64 rows per wave)
 constexpr int LSH_CB = 8;      // rotation columns per pass
+constexpr int LSH_BATCH = 4;   // row steps whose loads a wave issues together
 constexpr int SORT_T = 1024;   // threads of the sort kernel (16 waves)
 constexpr int SORT_W = SORT_T / 64;
+constexpr int SORT_STAGE = 16;  // chunks of bucket groups staged in LDS at a time
 constexpr int LSH_NB_LIMIT = 64;    // largest bucket count of the hash (rotation staged in LDS)
 constexpr int SORT_NB_LIMIT = 512;  // largest bucket count of the sort (per-wave group counts in LDS)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of L lanes (L = 8, 16 or 32), the result in every lane of the group: quad
+// swaps, then the mirror within 8 lanes and within 16 lanes (data-parallel moves on the vector ALU), then
+// a cross-row exchange for 32.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  if constexpr (L >= 16) v += dpp_move<0x140>(v);  // row_mirror
+  if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
 
 }  // namespace
 
 int lsh_max_nb() { return LSH_NB_LIMIT; }
 int sort_max_nb() { return SORT_NB_LIMIT; }
 
-// One thread per row. The head's rotation (d x nh floats, nh = nb / 2) is staged in LDS and read by
-// all lanes at the same address. Scores are accumulated over d in increasing order with fused
-// multiply-adds; the bucket is the first index of the maximum over [p_0 .. p_nh-1, -p_0 .. -p_nh-1].
+// A row is read by a group of L = 16-byte chunks per row lanes (16 lanes for bf16 at d = 128), so one
+// load instruction of a wave covers 64 / L whole rows, contiguous in memory; a wave issues the loads of
+// LSH_BATCH such steps before using them. The head's rotation (d x nh floats, nh = nb / 2) is staged in
+// LDS grouped by chunk, each chunk's block padded by 4 floats so that the L lanes of a group, which read
+// different chunks' blocks at the same time, fall into different banks. Each lane forms partial dot
+// products over its chunk (the rotation slice kept in registers when nh <= 8), the group sums them with
+// data-parallel lane moves (float32, a fixed order), and the group's first lane writes the first index of
+// the maximum over [p_0 .. p_nh-1, -p_0 .. -p_nh-1].
 template <typename T, int D>
 __global__ __launch_bounds__(LSH_T) void lsh_buckets_kernel(const T* __restrict__ x, const float* __restrict__ rot,
                                                             int H, int N, int Hr, int nh, int* __restrict__ out) {
-  __shared__ float r_lds[D * LSH_NB_LIMIT / 2];
+  constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int L = D / EPV;                 // lanes per row
+  constexpr int RPI = 64 / L;                // rows per wave per step
+  __shared__ __attribute__((aligned(16))) float r_lds[D * LSH_NB_LIMIT / 2 + 4 * L];
   const int nblk = (N + LSH_T - 1) / LSH_T;
   const int bh = (int)(blockIdx.x / nblk);
-  const int row = (int)(blockIdx.x % nblk) * LSH_T + (int)threadIdx.x;
+  const int row0 = (int)(blockIdx.x % nblk) * LSH_T;
   const float* rh = rot + (size_t)(Hr > 1 ? bh % H : 0) * D * nh;
-  for (int i = threadIdx.x; i < D * nh; i += LSH_T) r_lds[i] = rh[i];
+  const int SP = EPV * nh + 4;  // floats per chunk block in LDS
+  for (int i = threadIdx.x; i < D * nh; i += LSH_T) {
+    const int k = i / nh, c = i - k * nh;
+    r_lds[(k / EPV) * SP + (k % EPV) * nh + c] = rh[i];
+  }
   __syncthreads();
-  if (row >= N) return;
-  const T* xr = x + ((size_t)bh * N + row) * D;
-  float best_p = -INFINITY, best_n = -INFINITY;
-  int arg_p = 0, arg_n = 0;
-  for (int c0 = 0; c0 < nh; c0 += LSH_CB) {
-    float acc[LSH_CB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % L;  // this lane's chunk of the row
+  const float* rl = r_lds + sub * SP;
+  static_assert(L == 8 || L == 16 || L == 32, "lane groups the reduction supports");
+  const bool small = nh <= LSH_CB;  // the whole rotation slice of this lane fits in registers
+  float rreg[EPV][LSH_CB];
 #pragma unroll
-    for (int c = 0; c < LSH_CB; ++c) acc[c] = 0.f;
-    constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte load
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += EPV) {
+  for (int e = 0; e < EPV; ++e)
+#pragma unroll
+    for (int c = 0; c < LSH_CB; ++c) rreg[e][c] = (small && c < nh) ? rl[e * nh + c] : 0.f;
+  static_assert((64 / RPI) % LSH_BATCH == 0, "row steps per wave split into whole batches");
+  for (int it0 = 0; it0 < 64 / RPI; it0 += LSH_BATCH) {
+    i32x4 raw[LSH_BATCH];
+#pragma unroll
+    for (int u = 0; u < LSH_BATCH; ++u) {  // the batch's loads, all in flight together
+      const int r = row0 + wave * 64 + (it0 + u) * RPI + lane / L;
+      raw[u] = r < N ? *reinterpret_cast<const i32x4*>(x + ((size_t)bh * N + r) * D + sub * EPV)
+                     : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < LSH_BATCH; ++u) {
+      const int row = row0 + wave * 64 + (it0 + u) * RPI + lane / L;
       float xv[EPV];
       if constexpr (sizeof(T) == 2) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8*>(xr + k0);
+        const bf16x8 v = __builtin_bit_cast(bf16x8, raw[u]);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) xv[e] = (float)w[e];
+        for (int e = 0; e < EPV; ++e) xv[e] = (float)v[e];
       } else {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(xr + k0);
+        const f32x4 v = __builtin_bit_cast(f32x4, raw[u]);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) xv[e] = w[e];
+        for (int e = 0; e < EPV; ++e) xv[e] = v[e];
       }
+      float best_p = -INFINITY, best_n = -INFINITY;
+      int arg_p = 0, arg_n = 0;
+      for (int c0 = 0; c0 < nh; c0 += LSH_CB) {
+        float acc[LSH_CB];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float* rr = r_lds + (k0 + e) * nh + c0;
+        for (int c = 0; c < LSH_CB; ++c) acc[c] = 0.f;
+        if (small) {
 #pragma unroll
-        for (int c = 0; c < LSH_CB; ++c)
-          if (c0 + c < nh) acc[c] = fmaf(xv[e], rr[c], acc[c]);
+          for (int e = 0; e < EPV; ++e)
+#pragma unroll
+            for (int c = 0; c < LSH_CB; ++c) acc[c] = fmaf(xv[e], rreg[e][c], acc[c]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float* rr = rl + e * nh + c0;
+#pragma unroll
+            for (int c = 0; c < LSH_CB; ++c)
+              if (c0 + c < nh) acc[c] = fmaf(xv[e], rr[c], acc[c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < LSH_CB; ++c) acc[c] = group_sum<L>(acc[c]);
+#pragma unroll
+        for (int c = 0; c < LSH_CB; ++c) {
+          if (c0 + c < nh) {
+            if (acc[c] > best_p) { best_p = acc[c]; arg_p = c0 + c; }
+            if (-acc[c] > best_n) { best_n = -acc[c]; arg_n = c0 + c; }
+          }
+        }
       }
-    }
-#pragma unroll
-    for (int c = 0; c < LSH_CB; ++c) {
-      if (c0 + c < nh) {
-        if (acc[c] > best_p) { best_p = acc[c]; arg_p = c0 + c; }
-        if (-acc[c] > best_n) { best_n = -acc[c]; arg_n = c0 + c; }
-      }
+      if (row < N && sub == 0) out[(size_t)bh * N + row] = best_n > best_p ? nh + arg_n : arg_p;
     }
   }
-  out[(size_t)bh * N + row] = best_n > best_p ? nh + arg_n : arg_p;
 }
 
 // One workgroup per (b, h) row. Pass 1 counts each group (bucket, or nb for dropped tokens) of queries
 // and keys; the exclusive scans give the first sorted position of every group. Pass 2 sweeps the
-// positions 1024 at a time in increasing order: inside a wave the tokens of one group are ranked by a
-// ballot per distinct group, per-wave group counts in LDS give the offsets of earlier waves, and running
+// positions 1024 at a time in increasing order: inside a wave the tokens of one group are ranked with one
+// ballot per bit of the group id, per-wave group counts in LDS give the offsets of earlier waves, and running
 // bases carry the counts of earlier chunks. This keeps the sort stable, and it gives every key the number
-// of same-group queries at earlier positions, which is its lo.
+// of same-group queries at earlier positions, which is its lo. The bucket groups of SORT_STAGE chunks are
+// loaded into LDS (16 bits each) at once: the vector memory counter covers loads and stores alike, so
+// waiting for loads also waits for the scattered output stores, and staging makes that one wait per
+// SORT_STAGE chunks. The bases are double-buffered and the per-wave counts carry their chunk number
+// (count | chunk << 16), so two barriers per chunk suffice and nothing is cleared.
 __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restrict__ qb, const int* __restrict__ kb,
                                                              int N, int nb, int* __restrict__ qidx,
                                                              int* __restrict__ qpos, int* __restrict__ kidx,
@@ -97,24 +160,42 @@ __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restri
                                                              int* __restrict__ lte, int* __restrict__ uts,
                                                              int* __restrict__ ute) {
   constexpr int G_MAX = SORT_NB_LIMIT + 1;
-  __shared__ int qbase[G_MAX], kbase[G_MAX], qend[G_MAX];
-  __shared__ int qcnt[SORT_W][G_MAX], kcnt[SORT_W][G_MAX];
+  __shared__ int qbase[2][G_MAX], kbase[2][G_MAX], qend[G_MAX];
+  __shared__ unsigned qcnt[SORT_W][G_MAX], kcnt[SORT_W][G_MAX];
+  __shared__ uint16_t qg_lds[SORT_STAGE * SORT_T], kg_lds[SORT_STAGE * SORT_T];
   const int G = nb + 1;
+  const int nbits = 32 - __builtin_clz((unsigned)nb);  // bits of the largest group id, nb (>= 1)
   const size_t base = (size_t)blockIdx.x * N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   auto group = [&](int v) { return (v >= 0 && v < nb) ? v : nb; };
 
-  for (int g = tid; g < G; g += SORT_T) { qbase[g] = 0; kbase[g] = 0; }
+  for (int g = tid; g < G; g += SORT_T) { qbase[0][g] = 0; kbase[0][g] = 0; }
+  for (int i = tid; i < SORT_W * G_MAX; i += SORT_T) {
+    (&qcnt[0][0])[i] = 0xFFFFFFFFu;  // chunk tag 0xFFFF: no chunk
+    (&kcnt[0][0])[i] = 0xFFFFFFFFu;
+  }
   __syncthreads();
-  for (int j = tid; j < N; j += SORT_T) {
-    atomicAdd(&qbase[group(qb[base + j])], 1);
-    atomicAdd(&kbase[group(kb[base + j])], 1);
+  for (int j0 = tid; j0 < N; j0 += 4 * SORT_T) {
+    int vq[4], vk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * SORT_T;
+      vq[u] = j < N ? qb[base + j] : 0;
+      vk[u] = j < N ? kb[base + j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (j0 + u * SORT_T < N) {
+        atomicAdd(&qbase[0][group(vq[u])], 1);
+        atomicAdd(&kbase[0][group(vk[u])], 1);
+      }
+    }
   }
   __syncthreads();
   // exclusive scans: wave 0 for queries, wave 1 for keys (each lane owns a run of groups)
   if (wave < 2) {
-    int* h = wave == 0 ? qbase : kbase;
+    int* h = wave == 0 ? qbase[0] : kbase[0];
     const int per = (G + 63) / 64;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     int run = 0;
@@ -134,54 +215,64 @@ __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restri
     }
   }
 
-  for (int c0 = 0; c0 < N; c0 += SORT_T) {
-    __syncthreads();  // bases of the previous chunk updated, its counts consumed
-    for (int g = lane; g < G; g += 64) {
-      qcnt[wave][g] = 0;
-      kcnt[wave][g] = 0;
-    }
+  auto count_of = [](unsigned c, unsigned chunk) { return (c >> 16) == chunk ? (int)(c & 0xFFFFu) : 0; };
+  int par = 0;
+  unsigned chunk = 0;
+  for (int c0 = 0; c0 < N; c0 += SORT_T, ++chunk, par ^= 1) {
     const int j = c0 + tid;
     const bool valid = j < N;
-    const int gq = valid ? group(qb[base + j]) : -1;
-    const int gk = valid ? group(kb[base + j]) : -1;
-    // queries: rank among same-group lanes of this wave, and the wave's count per group
-    int rank_q = 0;
-    uint64_t active = __ballot(valid);
-    while (active != 0ull) {
-      const int lead = __builtin_ctzll(active);
-      const int v = __shfl(gq, lead, 64);
-      const uint64_t m = __ballot(gq == v);
-      if (gq == v) rank_q = __builtin_popcountll(m & lt_mask);
-      if (lane == lead) qcnt[wave][v] = __builtin_popcountll(m);
-      active &= ~m;
-    }
-    // keys: the same, plus the same-group queries at earlier lanes (earlier positions) of this wave
-    int rank_k = 0, q_before = 0;
-    active = __ballot(valid);
-    while (active != 0ull) {
-      const int lead = __builtin_ctzll(active);
-      const int v = __shfl(gk, lead, 64);
-      const uint64_t m = __ballot(gk == v);
-      const uint64_t mq = __ballot(gq == v);
-      if (gk == v) {
-        rank_k = __builtin_popcountll(m & lt_mask);
-        q_before = __builtin_popcountll(mq & lt_mask);
+    const int slot = (int)(chunk % SORT_STAGE);
+    if (slot == 0) {  // stage the groups of the next SORT_STAGE chunks
+      __syncthreads();  // the previous stage is consumed
+      int vq[SORT_STAGE], vk[SORT_STAGE];
+#pragma unroll
+      for (int u = 0; u < SORT_STAGE; ++u) {
+        const int jj = j + u * SORT_T;
+        vq[u] = jj < N ? qb[base + jj] : 0;
+        vk[u] = jj < N ? kb[base + jj] : 0;
       }
-      if (lane == lead) kcnt[wave][v] = __builtin_popcountll(m);
-      active &= ~m;
+#pragma unroll
+      for (int u = 0; u < SORT_STAGE; ++u) {
+        qg_lds[u * SORT_T + tid] = (uint16_t)group(vq[u]);
+        kg_lds[u * SORT_T + tid] = (uint16_t)group(vk[u]);
+      }
     }
+    __syncthreads();  // the previous chunk's counts and bases are consumed; the new bases are visible
+    const int gq = valid ? (int)qg_lds[slot * SORT_T + tid] : -1;
+    const int gk = valid ? (int)kg_lds[slot * SORT_T + tid] : -1;
+    // Same-group lane masks by one ballot per bit of the group id: a lane's mask is the AND over the
+    // bits of the ballot (bit set) or its complement (bit clear). The query-bit ballots also give, for
+    // each key, the queries of the key's group in this wave.
+    const uint64_t vmask = __ballot(valid);
+    uint64_t same_q = vmask, same_k = vmask, q_of_k = vmask;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t bq = __ballot(valid && ((gq >> bit) & 1));
+      const uint64_t bk = __ballot(valid && ((gk >> bit) & 1));
+      same_q &= ((gq >> bit) & 1) ? bq : ~bq;
+      same_k &= ((gk >> bit) & 1) ? bk : ~bk;
+      q_of_k &= ((gk >> bit) & 1) ? bq : ~bq;
+    }
+    const int rank_q = __builtin_popcountll(same_q & lt_mask);
+    const int rank_k = __builtin_popcountll(same_k & lt_mask);
+    const int q_before = __builtin_popcountll(q_of_k & lt_mask);
+    // the first lane of each group in this wave records the wave's count for it
+    if (valid && rank_q == 0) qcnt[wave][gq] = (chunk << 16) | (unsigned)__builtin_popcountll(same_q);
+    if (valid && rank_k == 0) kcnt[wave][gk] = (chunk << 16) | (unsigned)__builtin_popcountll(same_k);
     __syncthreads();
     if (valid) {
       int off_q = 0, off_k = 0, off_kq = 0;
-      for (int w = 0; w < wave; ++w) {
-        off_q += qcnt[w][gq];
-        off_k += kcnt[w][gk];
-        off_kq += qcnt[w][gk];
+#pragma unroll
+      for (int w = 0; w < SORT_W; ++w) {  // all reads issued together; earlier waves counted
+        const int a = count_of(qcnt[w][gq], chunk), b = count_of(kcnt[w][gk], chunk);
+        const int c = count_of(qcnt[w][gk], chunk);
+        off_q += w < wave ? a : 0;
+        off_k += w < wave ? b : 0;
+        off_kq += w < wave ? c : 0;
       }
-      const int pq = qbase[gq] + off_q + rank_q;
+      const int pq = qbase[par][gq] + off_q + rank_q;
       qidx[base + pq] = j;
       qpos[base + j] = pq;
-      const int pk = kbase[gk] + off_k + rank_k;
+      const int pk = kbase[par][gk] + off_k + rank_k;
       kidx[base + pk] = j;
       kpos[base + j] = pk;
       if (gk == nb) {  // dropped key: every row masked
@@ -191,21 +282,20 @@ __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restri
         lte[base + pk] = N;
       } else {
         uts[base + pk] = 0;
-        ute[base + pk] = qbase[gk] + off_kq + q_before;  // lo: first row of the group at or after j
-        lts[base + pk] = qend[gk];                       // N when the group ends last: canonical empty
+        ute[base + pk] = qbase[par][gk] + off_kq + q_before;  // lo: first row of the group at or after j
+        lts[base + pk] = qend[gk];                            // N when the group ends last: canonical empty
         lte[base + pk] = N;
       }
     }
-    __syncthreads();
     for (int g = tid; g < G; g += SORT_T) {
       int sq = 0, sk = 0;
 #pragma unroll
       for (int w = 0; w < SORT_W; ++w) {
-        sq += qcnt[w][g];
-        sk += kcnt[w][g];
+        sq += count_of(qcnt[w][g], chunk);
+        sk += count_of(kcnt[w][g], chunk);
       }
-      qbase[g] += sq;
-      kbase[g] += sk;
+      qbase[par ^ 1][g] = qbase[par][g] + sq;
+      kbase[par ^ 1][g] = kbase[par][g] + sk;
     }
   }
 }
