@@ -418,7 +418,8 @@ def main():
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "schedule": "longest-first" if use_sched else "default order",
         "parts_ms": {"fm_tile_bounds": round(float(parts_ms[0]), 4),
-                     "fm_tile_schedule": round(float(parts_ms[1]), 4), "fm_fwd": round(float(parts_ms[2]), 4),
+                     "fm_tile_schedule": round(float(parts_ms[1]), 4) if use_sched else None,
+                     "fm_fwd": round(float(parts_ms[2]), 4),
                      "fm_bwd": round(bwd_ms, 4)},
         "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[2] * 1e-3) / 1e12, 2),
                          "fm_bwd": round(bwd_tflops, 2)},
@@ -452,7 +453,8 @@ def main():
             ms = w2 * 1e3 / n
             sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
                            "U": int(wl.U), "fwd_ms": round(float(p2[2]), 3), "bwd_ms": round(float(p2[3]), 3),
-                           "bounds_ms": round(float(p2[0]), 4), "schedule_ms": round(float(p2[1]), 4),
+                           "bounds_ms": round(float(p2[0]), 4),
+                           "schedule_ms": round(float(p2[1] if use_sched else p0[1]), 4),
                            "finite": ok2,
                            ("ms_per_step_default_order" if use_sched else "ms_per_step_longest_first"):
                                round(w0 * 1e3 / n, 3),
