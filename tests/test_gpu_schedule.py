@@ -160,3 +160,27 @@ def test_fullsize_schedule_sampled(fm, name):
             assert qc[b, h, qt] == OS.query_unit_work(b64, spec.causal, N, N, 0, qt), ("query unit", b, h, qt)
         for kt in sorted(set(rng.integers(0, nk, size=6).tolist()) | {0, nk - 1}):
             assert kc[b, h, kt] == OS.key_unit_work(b128, spec.causal, N, N, 0, kt), ("key unit", b, h, kt)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_scheduled_row_blocks_bitwise_equal(fm, dtype, d):
+    """fm_fwd_rows / fm_bwd_rows with the row block's own schedule give the results of the default order."""
+    N = 1800
+    case = C.make_case(2, "causal_document", 1, 2, N, d, dtype)
+    print(f"\nscheduled row blocks {case.name}", flush=True)
+    vecs = C.device_vectors(case.spec)
+    bounds = fm.fm_tile_bounds(*vecs, 1, 1, N)
+    k, v = case.k.cuda(), case.v.cuda()
+    for a, b in ((0, 700), (700, 1333), (1333, N)):
+        q = case.q[:, :, a:b].contiguous().cuda()
+        do = case.do[:, :, a:b].contiguous().cuda()
+        s = fm.fm_tile_schedule(bounds, 1, 1, b - a, N, True, a)
+        runs = []
+        for sc in (None, s):
+            out, lse = fm.fm_fwd_rows(q, k, v, a, *vecs, bounds=bounds, sched=sc, causal=True, scale=case.scale)
+            dq, dk, dv = fm.fm_bwd_rows(q, k, v, out, do, lse, a, *vecs, bounds=bounds, sched=sc, causal=True,
+                                        scale=case.scale)
+            torch.cuda.synchronize()
+            runs.append([t.cpu() for t in (out, lse, dq, dk, dv)])
+        for x, y in zip(*runs):
+            assert torch.equal(x, y), (a, b)
