@@ -172,3 +172,46 @@ def test_hash_fullsize_sampled(fm, name):
         assert C.rel_fro(C.f64(gpu["dk"][b, h, cols]), r_dk) <= tol["grad"]
         assert C.rel_fro(C.f64(gpu["dv"][b, h, cols]), r_dv) <= tol["grad"]
         print(f"  head ({b},{h}) ok", flush=True)
+
+
+def test_hash_pipeline_graph_replays(fm):
+    """The whole hash pipeline captured in a HIP graph (torch.cuda.CUDAGraph; the library allocates nothing
+    and issues no memset): every replay, with eager work and synchronisations between replays, equals the
+    eager run bitwise (the pipeline has no atomics)."""
+    print("\nhash pipeline graph replays", flush=True)
+    B, H, N, d, nb = 1, 2, 1500, 128, 8
+    q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in W.make_tensors(2, 103, B, H, N, d))
+    R = torch.from_numpy(W.make_rotation(2, 103, H, d, nb)).cuda()
+    scale = d ** -0.5
+
+    def step():
+        qb = fm.fm_lsh_buckets(q, R, nb)
+        kb = fm.fm_lsh_buckets(k, R, nb)
+        qidx, qpos, kidx, kpos, vecs = fm.fm_bucket_sort(qb, kb, nb)
+        qs, dos = fm.fm_gather_rows(q, qidx), fm.fm_gather_rows(do, qidx)
+        ks, vs = fm.fm_gather_rows(k, kidx), fm.fm_gather_rows(v, kidx)
+        bounds = fm.fm_tile_bounds(*vecs, B, H, N)
+        outs, lse = fm.fm_fwd(qs, ks, vs, *vecs, bounds=bounds, causal=False, scale=scale)
+        dqs, dks, dvs = fm.fm_bwd(qs, ks, vs, outs, dos, lse, *vecs, bounds=bounds, causal=False, scale=scale)
+        return [fm.fm_gather_rows(outs, qpos), fm.fm_gather_rows(dqs, qpos), fm.fm_gather_rows(dks, kpos),
+                fm.fm_gather_rows(dvs, kpos), lse, qb, kb]
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm the allocator on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), rep
+        junk = (q.float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        del junk
