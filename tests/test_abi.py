@@ -192,3 +192,34 @@ def test_schedule_validation(lib):
     assert lib.fm_tile_schedule(A, 1, 1, 100, 0, 0, 1, B_, None) == fm.FM_ERR_INVALID
     assert lib.fm_tile_schedule(A, 1, 1, 100, 100, -1, 1, B_, None) == fm.FM_ERR_INVALID
     assert lib.fm_tile_schedule(A, 1, 1, 100, 100, (1 << 24) - 50, 1, B_, None) == fm.FM_ERR_INVALID
+
+
+def test_hash_validation(lib):
+    # fm_lsh_buckets(x, dtype, B, H, N, d, rot, Hr, nb, buckets, stream)
+    def lsh(**kw):
+        a = dict(x=A, dtype=fm.FM_BF16, B=1, H=2, N=100, d=128, rot=A, Hr=2, nb=16, out=B_)
+        a.update(kw)
+        return lib.fm_lsh_buckets(a["x"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["rot"], a["Hr"], a["nb"],
+                                  a["out"], None)
+    for name in ("x", "rot", "out"):
+        assert lsh(**{name: None}) == fm.FM_ERR_INVALID, name
+    assert lsh(nb=15) == fm.FM_ERR_INVALID          # odd
+    assert lsh(nb=0) == fm.FM_ERR_INVALID
+    assert lsh(nb=66) == fm.FM_ERR_INVALID          # above 64
+    assert lsh(Hr=3) == fm.FM_ERR_INVALID           # not 1 or H
+    assert lsh(x=P(0x100004)) == fm.FM_ERR_INVALID  # misaligned
+    assert lsh(d=96) == fm.FM_ERR_UNSUPPORTED
+    assert lsh(dtype=9) == fm.FM_ERR_UNSUPPORTED
+    assert lsh(N=0) == fm.FM_ERR_INVALID
+
+    # fm_bucket_sort(qb, kb, B, H, N, nb, qidx, qpos, kidx, kpos, lts, lte, uts, ute, stream)
+    def srt(nb=16, N=100, **kw):
+        p = dict(qb=A, kb=A, qidx=B_, qpos=B_, kidx=B_, kpos=B_, lts=B_, lte=B_, uts=B_, ute=B_)
+        p.update(kw)
+        return lib.fm_bucket_sort(p["qb"], p["kb"], 1, 2, N, nb, p["qidx"], p["qpos"], p["kidx"], p["kpos"],
+                                  p["lts"], p["lte"], p["uts"], p["ute"], None)
+    for name in ("qb", "kb", "qidx", "qpos", "kidx", "kpos", "lts", "lte", "uts", "ute"):
+        assert srt(**{name: None}) == fm.FM_ERR_INVALID, name
+    assert srt(nb=0) == fm.FM_ERR_INVALID
+    assert srt(nb=513) == fm.FM_ERR_INVALID
+    assert srt(N=(1 << 24) + 1) == fm.FM_ERR_INVALID
