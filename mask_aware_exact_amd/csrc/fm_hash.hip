@@ -25,6 +25,7 @@ constexpr int LSH_BATCH = 4;   // row steps whose loads a wave issues together
 constexpr int SORT_T = 1024;   // threads of the sort kernel (16 waves)
 constexpr int SORT_W = SORT_T / 64;
 constexpr int SORT_STAGE = 16;  // chunks of bucket groups staged in LDS at a time
+constexpr int SORT_SEG = 2048;  // least tokens per segment when a head's sort is split over workgroups
 constexpr int LSH_NB_LIMIT = 64;    // largest bucket count of the hash (rotation staged in LDS)
 constexpr int SORT_NB_LIMIT = 512;  // largest bucket count of the sort (per-wave group counts in LDS)
 
@@ -143,59 +144,56 @@ __global__ __launch_bounds__(LSH_T) void lsh_buckets_kernel(const T* __restrict_
   }
 }
 
-// One workgroup per (b, h) row. Pass 1 counts each group (bucket, or nb for dropped tokens) of queries
-// and keys; the exclusive scans give the first sorted position of every group. Pass 2 sweeps the
-// positions 1024 at a time in increasing order: inside a wave the tokens of one group are ranked with one
-// ballot per bit of the group id, per-wave group counts in LDS give the offsets of earlier waves, and running
-// bases carry the counts of earlier chunks. This keeps the sort stable, and it gives every key the number
-// of same-group queries at earlier positions, which is its lo. The bucket groups of SORT_STAGE chunks are
-// loaded into LDS (16 bits each) at once: the vector memory counter covers loads and stores alike, so
-// waiting for loads also waits for the scattered output stores, and staging makes that one wait per
-// SORT_STAGE chunks. The bases are double-buffered and the per-wave counts carry their chunk number
-// (count | chunk << 16), so two barriers per chunk suffice and nothing is cleared.
-__global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restrict__ qb, const int* __restrict__ kb,
-                                                             int N, int nb, int* __restrict__ qidx,
-                                                             int* __restrict__ qpos, int* __restrict__ kidx,
-                                                             int* __restrict__ kpos, int* __restrict__ lts,
-                                                             int* __restrict__ lte, int* __restrict__ uts,
-                                                             int* __restrict__ ute) {
+// Segment s of nseg equal parts of [0, N).
+__device__ __forceinline__ int seg_begin(int s, int N, int nseg) { return (int)((long)s * N / nseg); }
+
+// Split sort, pass 1: the group counts of one segment (queries, then keys) into the first 2 G entries of the
+// segment's own qpos range (a segment holds at least SORT_SEG >= 3 G positions).
+__global__ __launch_bounds__(256) void bucket_count_kernel(const int* __restrict__ qb, const int* __restrict__ kb, int N,
+                                                           int nb, int nseg, int* __restrict__ qpos) {
   constexpr int G_MAX = SORT_NB_LIMIT + 1;
-  __shared__ int qbase[2][G_MAX], kbase[2][G_MAX], qend[G_MAX];
-  __shared__ unsigned qcnt[SORT_W][G_MAX], kcnt[SORT_W][G_MAX];
-  __shared__ uint16_t qg_lds[SORT_STAGE * SORT_T], kg_lds[SORT_STAGE * SORT_T];
+  __shared__ int hq[G_MAX], hk[G_MAX];
   const int G = nb + 1;
-  const int nbits = 32 - __builtin_clz((unsigned)nb);  // bits of the largest group id, nb (>= 1)
+  const int row = (int)(blockIdx.x / nseg), seg = (int)(blockIdx.x % nseg);
+  const size_t base = (size_t)row * N;
+  const int s0 = seg_begin(seg, N, nseg), s1 = seg_begin(seg + 1, N, nseg);
+  for (int g = threadIdx.x; g < G; g += 256) { hq[g] = 0; hk[g] = 0; }
+  __syncthreads();
+  for (int j = s0 + (int)threadIdx.x; j < s1; j += 256) {
+    const int vq = qb[base + j], vk = kb[base + j];
+    atomicAdd(&hq[(vq >= 0 && vq < nb) ? vq : nb], 1);
+    atomicAdd(&hk[(vk >= 0 && vk < nb) ? vk : nb], 1);
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += 256) {
+    qpos[base + s0 + g] = hq[g];
+    qpos[base + s0 + G + g] = hk[g];
+  }
+}
+
+// Split sort, pass 2 (one workgroup per row): group totals, their exclusive scans (the first sorted position
+// of each group), and for every segment the position its first token of each group takes, replacing the
+// counts in place; the query group ends go to entries [2 G, 3 G) of every segment. Thread g alone reads
+// and writes column g of every segment.
+__global__ __launch_bounds__(1024) void bucket_scan_kernel(int N, int nb, int nseg, int* __restrict__ qpos) {
+  constexpr int G_MAX = SORT_NB_LIMIT + 1;
+  __shared__ int tq[G_MAX], tk[G_MAX], qe[G_MAX];
+  const int G = nb + 1;
   const size_t base = (size_t)blockIdx.x * N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  auto group = [&](int v) { return (v >= 0 && v < nb) ? v : nb; };
-
-  for (int g = tid; g < G; g += SORT_T) { qbase[0][g] = 0; kbase[0][g] = 0; }
-  for (int i = tid; i < SORT_W * G_MAX; i += SORT_T) {
-    (&qcnt[0][0])[i] = 0xFFFFFFFFu;  // chunk tag 0xFFFF: no chunk
-    (&kcnt[0][0])[i] = 0xFFFFFFFFu;
+  for (int g = tid; g < G; g += 1024) {
+    int sq = 0, sk = 0;
+    for (int sg = 0; sg < nseg; ++sg) {
+      const size_t o = base + seg_begin(sg, N, nseg);
+      sq += qpos[o + g];
+      sk += qpos[o + G + g];
+    }
+    tq[g] = sq;
+    tk[g] = sk;
   }
   __syncthreads();
-  for (int j0 = tid; j0 < N; j0 += 4 * SORT_T) {
-    int vq[4], vk[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * SORT_T;
-      vq[u] = j < N ? qb[base + j] : 0;
-      vk[u] = j < N ? kb[base + j] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (j0 + u * SORT_T < N) {
-        atomicAdd(&qbase[0][group(vq[u])], 1);
-        atomicAdd(&kbase[0][group(vk[u])], 1);
-      }
-    }
-  }
-  __syncthreads();
-  // exclusive scans: wave 0 for queries, wave 1 for keys (each lane owns a run of groups)
-  if (wave < 2) {
-    int* h = wave == 0 ? qbase[0] : kbase[0];
+  if (wave < 2) {  // exclusive scans: wave 0 queries, wave 1 keys
+    int* h = wave == 0 ? tq : tk;
     const int per = (G + 63) / 64;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     int run = 0;
@@ -210,17 +208,115 @@ __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restri
     for (int g = g0; g < g1; ++g) {
       const int c = h[g];
       h[g] = acc;
-      if (wave == 0) qend[g] = acc + c;
+      if (wave == 0) qe[g] = acc + c;
       acc += c;
+    }
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += 1024) {
+    int rq = tq[g], rk = tk[g];
+    for (int sg = 0; sg < nseg; ++sg) {
+      const size_t o = base + seg_begin(sg, N, nseg);
+      const int cq = qpos[o + g], ck = qpos[o + G + g];
+      qpos[o + g] = rq;
+      qpos[o + G + g] = rk;
+      qpos[o + 2 * G + g] = qe[g];
+      rq += cq;
+      rk += ck;
+    }
+  }
+}
+
+// One workgroup per (b, h) row. Pass 1 counts each group (bucket, or nb for dropped tokens) of queries
+// and keys; the exclusive scans give the first sorted position of every group. Pass 2 sweeps the
+// positions 1024 at a time in increasing order: inside a wave the tokens of one group are ranked with one
+// ballot per bit of the group id, per-wave group counts in LDS give the offsets of earlier waves, and running
+// bases carry the counts of earlier chunks. This keeps the sort stable, and it gives every key the number
+// of same-group queries at earlier positions, which is its lo. The bucket groups of SORT_STAGE chunks are
+// loaded into LDS (16 bits each) at once: the vector memory counter covers loads and stores alike, so
+// waiting for loads also waits for the scattered output stores, and staging makes that one wait per
+// SORT_STAGE chunks. The bases are double-buffered and the per-wave counts carry their chunk number
+// (count | chunk << 16), so two barriers per chunk suffice and nothing is cleared.
+__global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restrict__ qb, const int* __restrict__ kb,
+                                                             int N, int nb, int nseg, int* __restrict__ qidx,
+                                                             int* __restrict__ qpos, int* __restrict__ kidx,
+                                                             int* __restrict__ kpos, int* __restrict__ lts,
+                                                             int* __restrict__ lte, int* __restrict__ uts,
+                                                             int* __restrict__ ute) {
+  constexpr int G_MAX = SORT_NB_LIMIT + 1;
+  __shared__ int qbase[2][G_MAX], kbase[2][G_MAX], qend[G_MAX];
+  __shared__ unsigned qcnt[SORT_W][G_MAX], kcnt[SORT_W][G_MAX];
+  __shared__ uint16_t qg_lds[SORT_STAGE * SORT_T], kg_lds[SORT_STAGE * SORT_T];
+  const int G = nb + 1;
+  const int nbits = 32 - __builtin_clz((unsigned)nb);  // bits of the largest group id, nb (>= 1)
+  const int row = (int)(blockIdx.x / nseg), seg = (int)(blockIdx.x % nseg);
+  const size_t base = (size_t)row * N;
+  const int s0 = seg_begin(seg, N, nseg), s1 = seg_begin(seg + 1, N, nseg);  // this workgroup's positions
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  auto group = [&](int v) { return (v >= 0 && v < nb) ? v : nb; };
+
+  for (int i = tid; i < SORT_W * G_MAX; i += SORT_T) {
+    (&qcnt[0][0])[i] = 0xFFFFFFFFu;  // chunk tag 0xFFFF: no chunk
+    (&kcnt[0][0])[i] = 0xFFFFFFFFu;
+  }
+  if (nseg > 1) {
+    // bases of this segment and the group ends, left in the segment's own qpos range by the scan
+    for (int g = tid; g < G; g += SORT_T) {
+      qbase[0][g] = qpos[base + s0 + g];
+      kbase[0][g] = qpos[base + s0 + G + g];
+      qend[g] = qpos[base + s0 + 2 * G + g];
+    }
+  } else {  // one workgroup for the whole row: count and scan here
+    for (int g = tid; g < G; g += SORT_T) { qbase[0][g] = 0; kbase[0][g] = 0; }
+    __syncthreads();
+    for (int j0 = tid; j0 < N; j0 += 4 * SORT_T) {
+      int vq[4], vk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * SORT_T;
+        vq[u] = j < N ? qb[base + j] : 0;
+        vk[u] = j < N ? kb[base + j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j0 + u * SORT_T < N) {
+          atomicAdd(&qbase[0][group(vq[u])], 1);
+          atomicAdd(&kbase[0][group(vk[u])], 1);
+        }
+      }
+    }
+    __syncthreads();
+    // exclusive scans: wave 0 for queries, wave 1 for keys (each lane owns a run of groups)
+    if (wave < 2) {
+      int* h = wave == 0 ? qbase[0] : kbase[0];
+      const int per = (G + 63) / 64;
+      const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
+      int run = 0;
+      for (int g = g0; g < g1; ++g) run += h[g];
+      int incl = run;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int acc = incl - run;
+      for (int g = g0; g < g1; ++g) {
+        const int c = h[g];
+        h[g] = acc;
+        if (wave == 0) qend[g] = acc + c;
+        acc += c;
+      }
     }
   }
 
   auto count_of = [](unsigned c, unsigned chunk) { return (c >> 16) == chunk ? (int)(c & 0xFFFFu) : 0; };
   int par = 0;
   unsigned chunk = 0;
-  for (int c0 = 0; c0 < N; c0 += SORT_T, ++chunk, par ^= 1) {
+  __syncthreads();  // bases and group ends are in LDS before any position is written (qpos held them)
+  for (int c0 = s0; c0 < s1; c0 += SORT_T, ++chunk, par ^= 1) {
     const int j = c0 + tid;
-    const bool valid = j < N;
+    const bool valid = j < s1;
     const int slot = (int)(chunk % SORT_STAGE);
     if (slot == 0) {  // stage the groups of the next SORT_STAGE chunks
       __syncthreads();  // the previous stage is consumed
@@ -228,8 +324,8 @@ __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restri
 #pragma unroll
       for (int u = 0; u < SORT_STAGE; ++u) {
         const int jj = j + u * SORT_T;
-        vq[u] = jj < N ? qb[base + jj] : 0;
-        vk[u] = jj < N ? kb[base + jj] : 0;
+        vq[u] = jj < s1 ? qb[base + jj] : 0;
+        vk[u] = jj < s1 ? kb[base + jj] : 0;
       }
 #pragma unroll
       for (int u = 0; u < SORT_STAGE; ++u) {
@@ -324,8 +420,21 @@ hipError_t launch_lsh_buckets(bool bf16_in, int d, const void* x, const float* r
 
 hipError_t launch_bucket_sort(const int* qb, const int* kb, int rows, int N, int nb, int* qidx, int* qpos,
                               int* kidx, int* kpos, int* lts, int* lte, int* uts, int* ute, hipStream_t stream) {
-  hipLaunchKernelGGL(bucket_sort_kernel, dim3((unsigned)rows), dim3(SORT_T), 0, stream, qb, kb, N, nb, qidx, qpos,
-                     kidx, kpos, lts, lte, uts, ute);
+  // Long rows are split into segments of at least SORT_SEG positions, one workgroup each, after a count
+  // and a scan pass; short rows take one workgroup that counts and scans for itself.
+  const int nseg = N >= 2 * SORT_SEG ? N / SORT_SEG : 1;
+  static_assert(SORT_SEG >= 3 * (SORT_NB_LIMIT + 1), "a segment holds its counts, bases and the group ends");
+  if (nseg > 1) {
+    hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)((long)rows * nseg)), dim3(256), 0, stream, qb, kb, N, nb,
+                       nseg, qpos);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bucket_scan_kernel, dim3((unsigned)rows), dim3(1024), 0, stream, N, nb, nseg, qpos);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bucket_sort_kernel, dim3((unsigned)((long)rows * nseg)), dim3(SORT_T), 0, stream, qb, kb, N, nb,
+                     nseg, qidx, qpos, kidx, kpos, lts, lte, uts, ute);
   return hipGetLastError();
 }
 

@@ -64,7 +64,9 @@ def test_lsh_matches_oracle(fm, dtype, d, nb, Hr):
             _check_lsh(gb[b, h], C.f64(x[b, h]), R[h if Hr > 1 else 0].astype(np.float64))
 
 
-SORT_CASES = [(1, 1, 1, 4), (2, 2, 63, 3), (1, 2, 1000, 16), (2, 1, 2500, 512), (1, 1, 777, 1), (1, 3, 4097, 8)]
+# rows of 4096 positions or more are split into segments of at least 2048, one workgroup each
+SORT_CASES = [(1, 1, 1, 4), (2, 2, 63, 3), (1, 2, 1000, 16), (2, 1, 2500, 512), (1, 1, 777, 1), (1, 3, 4097, 8),
+              (1, 2, 10000, 512), (2, 1, 8192, 16), (1, 1, 12345, 1)]
 
 
 @pytest.mark.parametrize("B,H,N,nb", SORT_CASES)
