@@ -512,6 +512,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         }
       }
     } else {
+      // above the default priority of the other roles' arithmetic, below role 0's products
+      __builtin_amdgcn_s_setprio(1);
       if (qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
@@ -520,6 +522,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
       }
       interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();  // (B) P is in LDS
 
