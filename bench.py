@@ -138,6 +138,52 @@ class Workload:
         self.flop = self.flop_fwd + self.flop_bwd
 
 
+def unmasked_per_row(spec: W.MaskSpec, H: int) -> np.ndarray:
+    """int64 [N]: unmasked (row, key) pairs of each query row, summed over the H heads. Per column the
+    masked rows are the union of up to three intervals (causal [0, j), LT, UT); inclusion-exclusion over
+    them, accumulated as +-1 steps in a difference array over the rows, gives every row's masked count."""
+    N = spec.N
+    j = np.arange(N, dtype=np.int64)
+    zero = np.zeros(N, dtype=np.int64)
+    total = np.zeros(N, dtype=np.int64)
+    for b in range(spec.B):
+        for hm in range(spec.Hm):
+            ivs = [(zero, j if spec.causal else zero)]
+            for s_, e_ in ((spec.lts, spec.lte), (spec.uts, spec.ute)):
+                if s_ is None:
+                    ivs.append((zero, zero))
+                else:
+                    lo = np.clip(s_[b, hm].astype(np.int64), 0, N)
+                    ivs.append((lo, np.maximum(np.clip(e_[b, hm].astype(np.int64), 0, N), lo)))
+
+            def meet(x, y):
+                return np.maximum(x[0], y[0]), np.minimum(x[1], y[1])
+
+            A, Bv, Cv = ivs
+            diff = np.zeros(N + 1, dtype=np.int64)
+            for (lo, hi), w in ((A, 1), (Bv, 1), (Cv, 1), (meet(A, Bv), -1), (meet(A, Cv), -1), (meet(Bv, Cv), -1),
+                                (meet(meet(A, Bv), Cv), 1)):
+                ok = hi > lo
+                np.add.at(diff, lo[ok], w)
+                np.add.at(diff, hi[ok], -w)
+            masked = np.cumsum(diff[:N])
+            total += (N - masked) * (H if spec.Hm == 1 else 1)
+    return total
+
+
+def balanced_row_blocks(spec: W.MaskSpec, H: int, ranks: int, align: int = 128):
+    """Row-block boundaries that give each rank about the same number of unmasked pairs (the load-balancing
+    goal of the FlashMask-3 summary's balancer, on one GPU's row blocks), rounded to `align` rows."""
+    cum = np.cumsum(unmasked_per_row(spec, H))
+    cuts = [0]
+    for r in range(1, ranks):
+        c = int(np.searchsorted(cum, cum[-1] * r / ranks))
+        c = int(round(c / align)) * align
+        cuts.append(min(max(c, cuts[-1]), spec.N))
+    cuts.append(spec.N)
+    return cuts
+
+
 def time_workload(fm, wl: Workload, steps: int, warmup: int, use_sched: bool = False):
     """One step = fm_tile_bounds (when the mask has vectors), fm_tile_schedule (longest-first dispatch
     order, only with use_sched), fm_fwd, fm_bwd; all of it timed. Returns the wall time of the
@@ -501,6 +547,19 @@ def main():
         ms = [c["ms"] for c in cp]
         sweep["long_context_causal_document, context-parallel rank shares (8 ranks)"] = {
             "ranks": cp, "max_ms": max(ms), "mean_ms": round(sum(ms) / len(ms), 3),
+            "imbalance_max_over_mean": round(max(ms) / (sum(ms) / len(ms)), 3)}
+        # the same 8 shares with boundaries that balance the unmasked pairs per rank
+        cuts = balanced_row_blocks(wl.spec, wl.H, ranks)
+        cpb = []
+        for r in range(ranks):
+            a, b = cuts[r], cuts[r + 1]
+            t = time_rows(fm, wl, a, b, max(2, args.steps // 8), 1)
+            u = unmasked_pairs(wl.spec, wl.H, rows=(a, b))
+            cpb.append({"rank": r, "rows": [a, b], "ms": round(t * 1e3, 3), "U": int(u),
+                        "TFLOP/s": round(14.0 * wl.d * u / t / 1e12, 2)})
+        ms = [c["ms"] for c in cpb]
+        sweep["long_context_causal_document, context-parallel rank shares (8 ranks, balanced by unmasked pairs)"] = {
+            "ranks": cpb, "max_ms": max(ms), "mean_ms": round(sum(ms) / len(ms), 3),
             "imbalance_max_over_mean": round(max(ms) / (sum(ms) / len(ms)), 3)}
         del wl
         torch.cuda.empty_cache()
