@@ -188,9 +188,10 @@ fm_status fm_gather_rows(const void* x, fm_dtype dtype, int B, int H, int N, int
  * fm_lsh_buckets: Reformer-style geometric hash of each row of x [B, H, N, d] (dtype, 16-byte aligned):
  *   buckets[b, h, i] = the first index of the maximum of the nb values [x_i R_h, -x_i R_h], with the
  *   rotation R_h = rot[h] (Hr = H) or rot[0] (Hr = 1), float32 [Hr, d, nb / 2] row-major, a random matrix
- *   the caller draws. Dot products are float32 (per-lane fused multiply-adds over 16-byte chunks of the
- *   row, combined by a fixed butterfly), so rows whose top two values differ by less than float32
- *   rounding may get either bucket.
+ *   the caller draws. Dot products are float32. bf16 rows use matrix-core products with R split into
+ *   three bf16 parts (hi + mid + lo, within 2^-24 |R| of R), accumulated in float32. float32 rows use
+ *   per-lane fused multiply-adds over 16-byte chunks of the row, combined by a fixed butterfly. Rows
+ *   whose top two values differ by less than float32 rounding may get either bucket.
  *   Errors: FM_ERR_INVALID (NULL, sizes, Hr not in {1, H}, nb odd or outside [2, 64], x misaligned),
  *   FM_ERR_UNSUPPORTED (d, dtype), FM_ERR_LAUNCH.
  *

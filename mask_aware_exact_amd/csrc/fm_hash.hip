@@ -9,7 +9,8 @@
 // p). So the key's column is masked on UT = [0, lo_c) and LT = [qe_b, N), and the attention kernels run
 // unchanged (causal flag off).
 //   fm_lsh_buckets  bucket of each row: argmax of [x R, -x R] for a random R [d, nb/2] (Reformer-style
-//                   geometric hashing), float32 dot products; HBM-bound (2 d bytes read per bf16 row).
+//                   geometric hashing), float32 dot products (matrix-core products for bf16 rows);
+//                   HBM-bound (2 d bytes read per bf16 row).
 //   fm_bucket_sort  stable counting sort of queries and keys by bucket (out-of-range buckets form a
 //                   trailing dropped group that attends and is attended by nothing), the permutations
 //                   both ways, and the sorted problem's four vectors, in one sweep per head.
@@ -52,7 +53,7 @@ __device__ __forceinline__ float group_sum(float v) {
 int lsh_max_nb() { return LSH_NB_LIMIT; }
 int sort_max_nb() { return SORT_NB_LIMIT; }
 
-// A row is read by a group of L = 16-byte chunks per row lanes (16 lanes for bf16 at d = 128), so one
+// float32 rows: a row is read by a group of L = 16-byte chunks per row lanes (16 lanes at d = 64), so one
 // load instruction of a wave covers 64 / L whole rows, contiguous in memory; a wave issues the loads of
 // LSH_BATCH such steps before using them. The head's rotation (d x nh floats, nh = nb / 2) is staged in
 // LDS grouped by chunk, each chunk's block padded by 4 floats so that the L lanes of a group, which read
@@ -396,16 +397,94 @@ __global__ __launch_bounds__(SORT_T) void bucket_sort_kernel(const int* __restri
   }
 }
 
+// bf16 rows: the projections x R of 32 rows at a time as one matrix product. The rotation is the A operand
+// (rows = rotation columns c, zero past nh; k = d) and the row block the B operand (k = d, columns = rows).
+// R is split into three bf16 parts, hi = bf16(R), mid = bf16(R - hi), lo = bf16(R - hi - mid), which
+// leave less than 2^-24 |R| out; their products with the bf16 row are exact in float32 and accumulate in
+// float32 (hi in one accumulator, mid and lo in another). Lane (l32, g) then holds the 16 projections
+// c = 8 (r / 4) + 4 g + r % 4 of row l32, so the first index of the maximum takes 16 compares in the lane
+// and one exchange with lane ^ 32. The parts are staged once per workgroup in LDS in operand order
+// (lane-linear 16-byte reads), read one k step at a time, so that four waves per SIMD fit in the
+// registers to keep enough row loads in flight. Each wave takes one 32-row block.
+constexpr int LSHM_ROWS = 128;  // rows per workgroup: four waves of 32
+
+template <int D>
+__global__ __launch_bounds__(LSH_T) __attribute__((amdgpu_waves_per_eu(4))) void lsh_buckets_mfma_kernel(const bf16* __restrict__ x,
+                                                                 const float* __restrict__ rot, int H, int N, int Hr,
+                                                                 int nh, int* __restrict__ out) {
+  constexpr int NK = D / 16;  // k steps of one product
+  static_assert(NK % 4 == 0 || 4 % NK == 0, "the waves split the rotation's k steps evenly");
+  __shared__ __attribute__((aligned(16))) bf16x8 a_lds[3][NK][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int nblk = (N + LSHM_ROWS - 1) / LSHM_ROWS;
+  const int bh = (int)(blockIdx.x / nblk);
+  const int row = (int)(blockIdx.x % nblk) * LSHM_ROWS + wave * 32 + l32;  // this lane's row
+  const float* rh = rot + (size_t)(Hr > 1 ? bh % H : 0) * D * nh;
+  const bf16* xh = x + (size_t)bh * N * D;
+
+  // the row's fragments (rows past N read row N - 1; their buckets are not written)
+  bf16x8 xf[NK];
+  {
+    const int r = min(row, N - 1);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) xf[k] = load_kcontig_frag<bf16>(xh + (size_t)r * D + k * 16 + 8 * g);
+  }
+  for (int k = wave; k < NK; k += 4) {
+    bf16x8 hi, mid, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = l32 < nh ? rh[(size_t)(k * 16 + 8 * g + e) * nh + l32] : 0.f;
+      hi[e] = (bf16)v;
+      const float v1 = v - (float)hi[e];
+      mid[e] = (bf16)v1;
+      lo[e] = (bf16)(v1 - (float)mid[e]);
+    }
+    a_lds[0][k][lane] = hi;
+    a_lds[1][k][lane] = mid;
+    a_lds[2][k][lane] = lo;
+  }
+  __syncthreads();
+
+  {
+    f32x16 acc = zero16(), acc2 = zero16();
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      acc = MM<bf16>::mma(a_lds[0][k][lane], xf[k], acc);
+      acc2 = MM<bf16>::mma(a_lds[1][k][lane], xf[k], acc2);
+      acc2 = MM<bf16>::mma(a_lds[2][k][lane], xf[k], acc2);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next step's operand reads after these products
+    }
+    float best_p = -INFINITY, best_n = -INFINITY;
+    int arg_p = 0, arg_n = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {  // c increases with r: strict compares keep the first index
+      const int c = 8 * (r >> 2) + 4 * g + (r & 3);
+      const float v = acc[r] + acc2[r];
+      if (c < nh) {
+        if (v > best_p) { best_p = v; arg_p = c; }
+        if (-v > best_n) { best_n = -v; arg_n = c; }
+      }
+    }
+    const float op = __shfl_xor(best_p, 32, 64), on = __shfl_xor(best_n, 32, 64);
+    const int oap = __shfl_xor(arg_p, 32, 64), oan = __shfl_xor(arg_n, 32, 64);
+    if (op > best_p || (op == best_p && oap < arg_p)) { best_p = op; arg_p = oap; }
+    if (on > best_n || (on == best_n && oan < arg_n)) { best_n = on; arg_n = oan; }
+    if (g == 0 && row < N) out[(size_t)bh * N + row] = best_n > best_p ? nh + arg_n : arg_p;
+  }
+}
+
 hipError_t launch_lsh_buckets(bool bf16_in, int d, const void* x, const float* rot, int B, int H, int N, int Hr,
                               int nb, int* out, hipStream_t stream) {
   const long grid = (long)B * H * ((N + LSH_T - 1) / LSH_T);
+  const long grid_m = (long)B * H * ((N + LSHM_ROWS - 1) / LSHM_ROWS);
   const int nh = nb / 2;
   if (bf16_in) {
     if (d == 64)
-      hipLaunchKernelGGL((lsh_buckets_kernel<bf16, 64>), dim3((unsigned)grid), dim3(LSH_T), 0, stream,
+      hipLaunchKernelGGL((lsh_buckets_mfma_kernel<64>), dim3((unsigned)grid_m), dim3(LSH_T), 0, stream,
                          static_cast<const bf16*>(x), rot, H, N, Hr, nh, out);
     else
-      hipLaunchKernelGGL((lsh_buckets_kernel<bf16, 128>), dim3((unsigned)grid), dim3(LSH_T), 0, stream,
+      hipLaunchKernelGGL((lsh_buckets_mfma_kernel<128>), dim3((unsigned)grid_m), dim3(LSH_T), 0, stream,
                          static_cast<const bf16*>(x), rot, H, N, Hr, nh, out);
   } else {
     if (d == 64)

@@ -64,6 +64,21 @@ def test_lsh_matches_oracle(fm, dtype, d, nb, Hr):
             _check_lsh(gb[b, h], C.f64(x[b, h]), R[h if Hr > 1 else 0].astype(np.float64))
 
 
+@pytest.mark.parametrize("d,nb,N", [(128, 64, 1), (128, 64, 31), (64, 2, 129), (128, 2, 33), (64, 64, 300),
+                                    (128, 6, 128)])
+def test_lsh_bf16_edges_match_oracle(fm, d, nb, N):
+    """bf16 rows: every rotation width from one projection to 32, and row counts below, at and one past a
+    workgroup's 128 rows."""
+    print(f"\nlsh bf16 edges d{d} nb{nb} N{N}", flush=True)
+    B, H = 1, 3
+    x = torch.from_numpy(W.make_tensors(2, 300 + d + nb + N, B, H, N, d)[0]).to(torch.bfloat16)
+    R = W.make_rotation(2, 300 + nb, H, d, nb)
+    gb = fm.fm_lsh_buckets(x.cuda(), torch.from_numpy(R).cuda(), nb).cpu().numpy()
+    assert gb.min() >= 0 and gb.max() < nb
+    for h in range(H):
+        _check_lsh(gb[0, h], C.f64(x[0, h]), R[h].astype(np.float64))
+
+
 # rows of 4096 positions or more are split into segments of at least 2048, one workgroup each
 SORT_CASES = [(1, 1, 1, 4), (2, 2, 63, 3), (1, 2, 1000, 16), (2, 1, 2500, 512), (1, 1, 777, 1), (1, 3, 4097, 8),
               (1, 2, 10000, 512), (2, 1, 8192, 16), (1, 1, 12345, 1)]
