@@ -174,38 +174,53 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int* __restrict
 
 // Split sort, pass 2 (one workgroup per row): group totals, their exclusive scans (the first sorted position
 // of each group), and for every segment the position its first token of each group takes, replacing the
-// counts in place; the query group ends go to entries [2 G, 3 G) of every segment. Thread g alone reads
-// and writes column g of every segment.
+// counts in place; the query group ends go to entries [2 G, 3 G) of every segment. Column j < 2 G of the
+// counts (queries at j < G, keys at j >= G) is the work of S lanes of a wave, S the segment count rounded
+// up to a power of two and at most 64, with the lanes over S segments at a time: a prefix sum over the S
+// lanes turns the counts into the positions before the segment within the group, written in place, and
+// the last lane's running sum is the group total. After the scans over groups, the same lanes add each
+// group's first position. Every entry is read and written by one lane.
+template <int W>
+__device__ __forceinline__ int group_incl_sum(int v, int sl, int S) {  // over aligned groups of S lanes
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) {
+    const int t = __shfl_up(v, o, S);
+    if (o < S && sl >= o) v += t;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(int N, int nb, int nseg, int* __restrict__ qpos) {
   constexpr int G_MAX = SORT_NB_LIMIT + 1;
-  __shared__ int tq[G_MAX], tk[G_MAX], qe[G_MAX];
+  __shared__ int tot[2 * G_MAX], qe[G_MAX];
   const int G = nb + 1;
   const size_t base = (size_t)blockIdx.x * N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int g = tid; g < G; g += 1024) {
-    int sq = 0, sk = 0;
-    for (int sg = 0; sg < nseg; ++sg) {
-      const size_t o = base + seg_begin(sg, N, nseg);
-      sq += qpos[o + g];
-      sk += qpos[o + G + g];
+  const int S = nseg >= 64 ? 64 : 1 << (32 - __builtin_clz((unsigned)(nseg - 1) | 1u));  // lanes per column
+  const int cpw = 64 / S;  // columns per wave at a time
+  const int sub = lane / S, sl = lane % S;
+  for (int j0 = wave * cpw; j0 < 2 * G; j0 += 16 * cpw) {
+    const int j = j0 + sub;
+    int carry = 0;
+    for (int s0 = 0; s0 < nseg; s0 += S) {
+      const int sg = s0 + sl;
+      const bool live = j < 2 * G && sg < nseg;
+      const size_t o = base + seg_begin(min(sg, nseg - 1), N, nseg) + min(j, 2 * G - 1);
+      const int c = live ? qpos[o] : 0;
+      const int incl = group_incl_sum<64>(c, sl, S);
+      if (live) qpos[o] = carry + incl - c;
+      carry += __shfl(incl, S - 1, S);
     }
-    tq[g] = sq;
-    tk[g] = sk;
+    if (j < 2 * G && sl == 0) tot[j] = carry;
   }
   __syncthreads();
-  if (wave < 2) {  // exclusive scans: wave 0 queries, wave 1 keys
-    int* h = wave == 0 ? tq : tk;
+  if (wave < 2) {  // exclusive scans over groups: wave 0 queries, wave 1 keys
+    int* h = tot + wave * G;
     const int per = (G + 63) / 64;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     int run = 0;
     for (int g = g0; g < g1; ++g) run += h[g];
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    int acc = incl - run;
+    int acc = group_incl_sum<64>(run, lane, 64) - run;
     for (int g = g0; g < g1; ++g) {
       const int c = h[g];
       h[g] = acc;
@@ -214,16 +229,17 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(int N, int nb, int ns
     }
   }
   __syncthreads();
-  for (int g = tid; g < G; g += 1024) {
-    int rq = tq[g], rk = tk[g];
-    for (int sg = 0; sg < nseg; ++sg) {
-      const size_t o = base + seg_begin(sg, N, nseg);
-      const int cq = qpos[o + g], ck = qpos[o + G + g];
-      qpos[o + g] = rq;
-      qpos[o + G + g] = rk;
-      qpos[o + 2 * G + g] = qe[g];
-      rq += cq;
-      rk += ck;
+  for (int j0 = wave * cpw; j0 < 2 * G; j0 += 16 * cpw) {
+    const int j = j0 + sub;
+    if (j >= 2 * G) continue;
+    const int start = tot[j];
+    for (int s0 = 0; s0 < nseg; s0 += S) {
+      const int sg = s0 + sl;
+      if (sg < nseg) {
+        const size_t o = base + seg_begin(sg, N, nseg);
+        qpos[o + j] += start;
+        if (j < G) qpos[o + 2 * G + j] = qe[j];
+      }
     }
   }
 }
