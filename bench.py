@@ -325,7 +325,7 @@ class HashWorkload:
 def time_hash_workload(fm, wl: HashWorkload, steps: int, warmup: int, graph: bool = False):
     """One step: fm_lsh_buckets of Q and K, fm_bucket_sort, fm_gather_rows of Q, K, V, dO into bucket
     order, fm_tile_bounds, fm_fwd and fm_bwd (no causal flag), fm_gather_rows of out, dq, dk, dv back.
-    All of it is timed. U is counted from the reordered problem's vectors after the warmup. With `graph`
+    All of it is timed. U is counted afterwards from the reordered problem's vectors. With `graph`
     the 16 launches of a step are captured once in a HIP graph and the timed steps are graph replays (the
     library allocates nothing and issues no memset, so the step replays as captured); on this stack the
     replays measured slower than the eager launches, which already run back to back, so eager is the
@@ -362,19 +362,17 @@ def time_hash_workload(fm, wl: HashWorkload, steps: int, warmup: int, graph: boo
         return vecs
 
     for _ in range(warmup):
-        vecs = step()
+        step()
     torch.cuda.synchronize()
-    lts, _, _, ute = vecs
-    U = int(torch.clamp(lts.long() - ute.long(), min=0).sum())
     run = step
     if graph:
-        ref = out.clone()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        ref = out.clone()  # the eager step's result, which every replay must reproduce
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step()
@@ -387,8 +385,14 @@ def time_hash_workload(fm, wl: HashWorkload, steps: int, warmup: int, graph: boo
     for _ in range(steps):
         run()
     torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
     ok = bool(torch.isfinite(out.float()).all() and torch.isfinite(dk.float()).all())
-    return (time.perf_counter() - t0) / steps, U, ok
+    # U from the reordered problem's vectors (untimed; the same buckets as every timed step)
+    fm.fm_lsh_buckets(wl.q, wl.rot, wl.nb, out=qb)
+    fm.fm_lsh_buckets(wl.k, wl.rot, wl.nb, out=kb)
+    lts, _, _, ute = fm.fm_bucket_sort(qb, kb, wl.nb)[4]
+    U = int(torch.clamp(lts.long() - ute.long(), min=0).sum())
+    return dt, U, ok
 
 
 def cpu_baseline(wl: Workload, budget_heads: int, max_tokens: int):
