@@ -130,22 +130,43 @@ __global__ __launch_bounds__(CT) void compact_keys_kernel(const int* __restrict_
   if (tid == 0) counts[row] = bad_any ? -1 : kept_before;
 }
 
-// y[b, h, r, :] = x[b, h, idx[b, hm, r], :], or zero where idx is negative: one 16-byte chunk per
-// thread (cpr chunks per row), grid-stride.
+// y[b, h, r, :] = x[b, h, idx[b, hm, r], :], or zero where idx is outside [0, N). A task is RPB rows of one
+// (b, h); thread t moves 16-byte chunk t % CPR of rows t / CPR + k * (256 / CPR), k < GK, loading the GK
+// indices, then the GK chunks, then storing them, so each thread has GK independent copies in flight.
+// CPR (chunks per row) is 8, 16 or 32, so the row and chunk of a thread are shifts, not divisions.
+constexpr int GK = 4;
+
+template <int CPR>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x, const int* __restrict__ idx,
-                                                          int H, int Hm, int N, int cpr, long total,
+                                                          int H, int Hm, int N, int nrb, long ntask,
                                                           char* __restrict__ y) {
-  for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < total; c += (long)gridDim.x * 256) {
-    const long wid = c / cpr;
-    const int piece = (int)(c - wid * cpr);
-    const int r = (int)(wid % N);
-    const long bh = wid / N;
+  constexpr int RPS = 256 / CPR;  // rows per step of the workgroup
+  constexpr int RPB = RPS * GK;   // rows per task
+  const int piece = threadIdx.x % CPR, rl = threadIdx.x / CPR;
+  for (long t = blockIdx.x; t < ntask; t += gridDim.x) {
+    const long bh = t / nrb;
+    const int r0 = (int)(t - bh * nrb) * RPB + rl;
     const int b = (int)(bh / H), h = (int)(bh % H);
-    const int hm = Hm > 1 ? h : 0;
-    const int src = idx[((size_t)b * Hm + hm) * N + r];
-    i32x4 v = {0, 0, 0, 0};
-    if (src >= 0 && src < N) v = *reinterpret_cast<const i32x4*>(x + (((size_t)bh * N + src) * cpr + piece) * 16);
-    *reinterpret_cast<i32x4*>(y + (size_t)c * 16) = v;
+    const int* ih = idx + ((size_t)b * Hm + (Hm > 1 ? h : 0)) * N;
+    const char* xh = x + (size_t)bh * N * (CPR * 16);
+    char* yh = y + (size_t)bh * N * (CPR * 16);
+    int src[GK];
+#pragma unroll
+    for (int k = 0; k < GK; ++k) {
+      const int r = r0 + k * RPS;
+      src[k] = r < N ? ih[r] : -1;
+    }
+    i32x4 v[GK];
+#pragma unroll
+    for (int k = 0; k < GK; ++k) {
+      v[k] = i32x4{0, 0, 0, 0};
+      if (src[k] >= 0 && src[k] < N) v[k] = *reinterpret_cast<const i32x4*>(xh + ((size_t)src[k] * CPR + piece) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < GK; ++k) {
+      const int r = r0 + k * RPS;
+      if (r < N) *reinterpret_cast<i32x4*>(yh + ((size_t)r * CPR + piece) * 16) = v[k];
+    }
   }
 }
 
@@ -160,10 +181,20 @@ hipError_t launch_compact_keys(const int* lts, const int* lte, const int* uts, c
 hipError_t launch_gather_rows(const void* x, const int* idx, int B, int H, int Hm, int N, int row_bytes, void* y,
                               hipStream_t stream) {
   const int cpr = row_bytes / 16;
-  const long total = (long)B * H * N * cpr;
-  const long blocks = min((total + 255) / 256, 256L * 1024);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const char*>(x), idx, H, Hm, N, cpr, total, static_cast<char*>(y));
+  const int rpb = 256 / cpr * GK;
+  const int nrb = (N + rpb - 1) / rpb;
+  const long ntask = (long)B * H * nrb;
+  const unsigned blocks = (unsigned)min(ntask, 1L << 20);
+  const char* xs = static_cast<const char*>(x);
+  char* ys = static_cast<char*>(y);
+  if (cpr == 8)
+    hipLaunchKernelGGL(gather_rows_kernel<8>, dim3(blocks), dim3(256), 0, stream, xs, idx, H, Hm, N, nrb, ntask, ys);
+  else if (cpr == 16)
+    hipLaunchKernelGGL(gather_rows_kernel<16>, dim3(blocks), dim3(256), 0, stream, xs, idx, H, Hm, N, nrb, ntask, ys);
+  else if (cpr == 32)
+    hipLaunchKernelGGL(gather_rows_kernel<32>, dim3(blocks), dim3(256), 0, stream, xs, idx, H, Hm, N, nrb, ntask, ys);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
