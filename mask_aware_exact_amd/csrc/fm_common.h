@@ -181,11 +181,13 @@ __device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int row_end
 // query rows, one row per lane): lane c forms the masked-row word of key column c0 + c for the rows
 // q0 .. q0 + 31 and stores it in the wave's own 64-word LDS row; the wave then reads back the words of
 // the columns its registers hold. LDS operations of one wave run in order, and the wave-scope fences
-// keep the compiler from moving the read-back above the store.
-__device__ __forceinline__ void tile_column_words(uint32_t* cw, const i32x4* vec, int q0, int c0, int row_end, int nk,
+// keep the compiler from moving the read-back above the store. `vec` holds the tile's vectors as
+// int [4][64]: LTS, LTE, UTS, UTE of its 64 columns.
+__device__ __forceinline__ void tile_column_words(uint32_t* cw, const int* vec, int q0, int c0, int row_end, int nk,
                                                   bool causal, bool has_lt, bool has_ut, int lane) {
-  const i32x4 mv = vec[lane];
-  cw[lane] = masked_row_bits32(q0, c0 + lane, row_end, nk, causal, has_lt, has_ut, mv[0], mv[1], mv[2], mv[3]);
+  const int lts = has_lt ? vec[lane] : 0, lte = has_lt ? vec[64 + lane] : 0;
+  const int uts = has_ut ? vec[128 + lane] : 0, ute = has_ut ? vec[192 + lane] : 0;
+  cw[lane] = masked_row_bits32(q0, c0 + lane, row_end, nk, causal, has_lt, has_ut, lts, lte, uts, ute);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -401,6 +403,11 @@ __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uin
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
 
+// Direct global-to-LDS load of 4 bytes per lane (256 bytes per wave instruction, lane-linear at `lds`).
+__device__ __forceinline__ void lds_copy4(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
+}
+
 // LDS byte address of a pointer into shared memory, made wave-uniform.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
@@ -441,6 +448,52 @@ __device__ __forceinline__ void copy_tile_async(bf16* tile, const bf16* __restri
     }
   }
 }
+
+// Direct global-to-LDS copy of the 64 columns c0 .. c0 + 63 of one mask vector row into dst[64]; columns
+// at or past n read column n - 1 (the kernels mask columns past n). `row` must be wave-uniform.
+__device__ __forceinline__ void copy_vector_slice(int* dst, const int* row, int c0, int n, int lane) {
+  lds_copy4(row, (uint32_t)min(c0 + lane, n - 1) * 4u, lds_addr(dst));
+}
+
+// One wave per vector: wave w of the first four copies LTS, LTE, UTS, UTE (as present) of the 64 columns
+// from c0 into vec[w][64]. `w` must be wave-uniform.
+__device__ __forceinline__ void copy_tile_vectors(int (*vec)[64], const int* lts, const int* lte, const int* uts,
+                                                  const int* ute, size_t vrow, int c0, int n, int w, int lane) {
+  const int* src = w == 0 ? lts : w == 1 ? lte : w == 2 ? uts : ute;
+  if (w < 4 && src != nullptr) copy_vector_slice(vec[w], src + vrow, c0, n, lane);
+}
+
+// The same copy as copy_tile_async, split into this wave's instructions so that the caller can spread
+// them between matrix products: prep() computes the addresses, issue(k) sends instruction k (k a
+// compile-time value after unrolling). Every lane's offset is clamped to its chunk of row nrows - 1,
+// which covers the ragged last tile without a branch.
+template <int D, int ROWS, int NW>
+struct TileCopy {
+  static constexpr int RB = D * 2;
+  static constexpr int RPI = 1024 / RB;
+  static constexpr int NI = ROWS / RPI;
+  static constexpr int NK = NI / NW;  // instructions per wave
+  static constexpr int CPW = RB / 16;
+  static constexpr uint32_t STEP = NW * RPI * RB;
+  static_assert(ROWS % RPI == 0 && NI % NW == 0, "the tile must split evenly over the waves");
+  static_assert((NW * RPI) % 16 == 0, "the swizzle key of a lane's row must not change between instructions");
+  const char* gb;  // wave-uniform: the tile's first row
+  uint32_t lds0;   // wave-uniform: LDS address of this wave's first instruction
+  uint32_t off0;   // lane: byte offset of its chunk for instruction 0
+  uint32_t lim;    // lane: byte offset of the same chunk position in row nrows - 1
+  __device__ __forceinline__ void prep(bf16* tile, const bf16* __restrict__ g, int row0, int nrows, int wave,
+                                       int lane) {
+    const int rl = wave * RPI + lane / CPW;
+    const int col = ((lane % CPW) ^ swz_key<D>(rl)) << 4;
+    gb = reinterpret_cast<const char*>(g + (size_t)row0 * D);
+    lds0 = lds_addr(tile) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+    off0 = (uint32_t)(rl * RB + col);
+    lim = (uint32_t)((nrows - 1 - row0) * RB + col);
+  }
+  __device__ __forceinline__ void issue(int k) const {
+    lds_copy16(gb, min(off0 + (uint32_t)k * STEP, lim), lds0 + (uint32_t)k * (NW * 1024u));
+  }
+};
 
 // 16-byte global/LDS copy helpers.
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }

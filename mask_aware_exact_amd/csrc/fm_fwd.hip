@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int VLP = SWZ ? D : VPITCH;
   __shared__ __attribute__((aligned(16))) T k_lds[2][BC * KLP];
   __shared__ __attribute__((aligned(16))) T v_lds[2][BC * VLP];
-  __shared__ __attribute__((aligned(16))) i32x4 vec_lds[2][BC];
+  __shared__ __attribute__((aligned(16))) int vec_lds[2][4][BC];  // LTS, LTE, UTS, UTE of the tile's columns
   __shared__ __attribute__((aligned(16))) uint32_t cw_lds[4][BC];  // per wave: masked-row words of a tile
 
   const int tid = threadIdx.x;
@@ -135,11 +135,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int nkt = (N + BC - 1) / BC;
   const int kt_end = causal ? min(nkt, (g1 - 1) / BC + 1) : nkt;
 
-  // Next tile: K / V (bf16: straight into LDS buffer `dst`; float: into staging registers) and the
-  // tile's mask vectors (registers).
+  // Next tile: K / V and the tile's mask vectors. bf16: straight into LDS buffer `dst` by direct copies
+  // (one vector per wave); float: into staging registers, stored by stash().
   constexpr int CHR = SWZ ? 1 : CH;
   i32x4 kr[CHR], vr[CHR];
   i32x4 mr = {0, 0, 0, 0};
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto fetch_vectors = [&](int kt, int dst) {
+    copy_tile_vectors(vec_lds[dst], a.lts, a.lte, a.uts, a.ute, vrow, kt * BC, N, wv, lane);
+  };
   auto fetch = [&](int kt, int dst) {
     const int c0 = kt * BC;
     if constexpr (SWZ) {
@@ -147,6 +151,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                                 lane);
       copy_tile_async<D, BC, 4>(reinterpret_cast<bf16*>(v_lds[dst]), reinterpret_cast<const bf16*>(vg), c0, N, wave,
                                 lane);
+      fetch_vectors(kt, dst);
     } else {
 #pragma unroll
       for (int it = 0; it < CH; ++it) {
@@ -156,13 +161,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         kr[it] = ld16(reinterpret_cast<const char*>(kg + rr * D) + cc * 16);
         vr[it] = ld16(reinterpret_cast<const char*>(vg + rr * D) + cc * 16);
       }
-    }
-    if (tid < BC) {
-      const int j = c0 + tid;
-      mr = i32x4{0, 0, 0, 0};
-      if (j < N) {
-        if (has_lt) { mr[0] = a.lts[vrow + j]; mr[1] = a.lte[vrow + j]; }
-        if (has_ut) { mr[2] = a.uts[vrow + j]; mr[3] = a.ute[vrow + j]; }
+      if (tid < BC) {
+        const int j = c0 + tid;
+        mr = i32x4{0, 0, 0, 0};
+        if (j < N) {
+          if (has_lt) { mr[0] = a.lts[vrow + j]; mr[1] = a.lte[vrow + j]; }
+          if (has_ut) { mr[2] = a.uts[vrow + j]; mr[3] = a.ute[vrow + j]; }
+        }
       }
     }
   };
@@ -175,8 +180,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         st16(reinterpret_cast<char*>(&k_lds[buf][r * PITCH]) + cc * 16, kr[it]);
         st16(reinterpret_cast<char*>(&v_lds[buf][r * VPITCH]) + cc * 16, vr[it]);
       }
+      if (tid < BC) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vec_lds[buf][e][tid] = mr[e];
+      }
     }
-    if (tid < BC) vec_lds[buf][tid] = mr;
   };
   SwzRowReads<D> krd;
   SwzColReads<D> vcd;
@@ -201,7 +209,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();
     const int kt_next = next_live_tile(win, kt + 1, kt_end, class_of, lane);
-    if (kt_next < kt_end) fetch(kt_next, buf ^ 1);
+    // bf16: the next tile's copies go out one at a time between the score products below, so that they
+    // queue while the matrix cores work instead of holding up the products. Without a next tile the
+    // current one is copied into the other buffer, which is never read, so the sequence is the same.
+    TileCopy<D, BC, 4> kcp, vcp;
+    if constexpr (SWZ) {
+      const int cn = (kt_next < kt_end ? kt_next : kt) * BC;
+      kcp.prep(reinterpret_cast<bf16*>(k_lds[buf ^ 1]), reinterpret_cast<const bf16*>(kg), cn, N, wave, lane);
+      vcp.prep(reinterpret_cast<bf16*>(v_lds[buf ^ 1]), reinterpret_cast<const bf16*>(vg), cn, N, wave, lane);
+      if (kt_next < kt_end) fetch_vectors(kt_next, buf ^ 1);
+    } else {
+      if (kt_next < kt_end) fetch(kt_next, buf ^ 1);
+    }
 
     const T* kt_lds = k_lds[buf];
     const T* vt_lds = v_lds[buf];
@@ -214,8 +233,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int jb = 0; jb < 2; ++jb) {
       s[jb] = zero16();
       if constexpr (SWZ) {
+        constexpr int NC = 2 * TileCopy<D, BC, 4>::NK;  // copies, one after every other product
+        static_assert(NC == Tr::NQF, "one copy per two score products");
 #pragma unroll
-        for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
+        for (int c = 0; c < Tr::NQF; ++c) {
+          s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
+          if (c & 1) {
+            const int k = (jb * Tr::NQF + c) >> 1;
+            if (k < NC / 2) kcp.issue(k); else vcp.issue(k - NC / 2);
+          }
+        }
       } else {
         const T* krow = kt_lds + (jb * 32 + l32) * PITCH + g * M::E;
 #pragma unroll
@@ -228,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
     float mx = -INFINITY;
     if (need_mask) {
-      tile_column_words(cw_lds[wave], vec_lds[buf], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut, lane);
+      tile_column_words(cw_lds[wave], &vec_lds[buf][0][0], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut, lane);
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -296,6 +323,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     buf ^= 1;
   }
 
+  if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // Epilogue: out = O / l, lse = m_ref * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (row < Nq) {
