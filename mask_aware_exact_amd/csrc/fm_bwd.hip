@@ -438,14 +438,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // read row N - 1, which gets lse = +inf below and so contributes nothing), lse and D into registers.
   float lr = 0.f, ddr = 0.f;
   int l_row = 0;
-  auto fetch = [&](int qt, int qslot, int dslot) {
-    const int q0 = qt * BR;
+  auto fetch_rows = [&](int qt) {
     if (tid < BR) {
-      l_row = q0 + tid;
+      l_row = qt * BR + tid;
       const int i = min(l_row, Nq - 1);
       lr = lseg[i];
       ddr = ddg[i];
     }
+  };
+  auto fetch = [&](int qt, int qslot, int dslot) {
+    const int q0 = qt * BR;
+    fetch_rows(qt);
     copy_tile_async<D, BR, 8>(q_lds + qslot * TILE, qg, q0, Nq, wave, lane);
     copy_tile_async<D, BR, 8>(do_lds + dslot * TILE, dog, q0, Nq, wave, lane);
   };
@@ -488,7 +491,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();  // (A) the tile is in LDS; every wave is past the previous tile's work
     const int qt_next = next_live_tile(win, qt + 1, nq, class_of, lane);
-    if (qt_next < nq) fetch(qt_next, qs == 2 ? 0 : qs + 1, ds ^ 1);
+    // The next tile's Q and dO copies go out one at a time between the score (role 0) or dP (role 1)
+    // products below, so that they queue while the matrix cores work. Without a next tile the current
+    // one is copied into the free slots, which are never read, so the sequence is the same.
+    TileCopy<D, BR, 8> cp;
+    const int qn = (qt_next < nq ? qt_next : qt) * BR;
+    cp.prep(q_lds + (qs == 2 ? 0 : qs + 1) * TILE, qg, qn, Nq, wave, lane);
+    const uint32_t dlds0 = lds_addr(do_lds + (ds ^ 1) * TILE) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+    const char* dgb = reinterpret_cast<const char*>(dog + (size_t)qn * D);
+    constexpr int NCP = 2 * TileCopy<D, BR, 8>::NK;  // copies per wave
+    constexpr int NMP = 2 * Tr::NKF;                 // products in the block that carries them
+    static_assert(NMP % NCP == 0, "copies must spread evenly over the products");
+    auto copy_after = [&](int m) {  // after product m (compile-time after unrolling)
+      if ((m + 1) % (NMP / NCP) == 0) {
+        const int k = (m + 1) / (NMP / NCP) - 1;
+        if (k < NCP / 2) cp.issue(k); else cp.issue_to(dgb, dlds0, k - NCP / 2);
+      }
+    };
+    if (qt_next < nq) fetch_rows(qt_next);
 
     const bf16* qb = q_lds + qs * TILE;
     const bf16* dob = do_lds + ds * TILE;
@@ -503,7 +523,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int ib = 0; ib < 2; ++ib) {
         x[ib] = zero16();
 #pragma unroll
-        for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(qb, ib, c), xf[c], x[ib]);
+        for (int c = 0; c < Tr::NKF; ++c) {
+          x[ib] = M::mma(rrd.read(qb, ib, c), xf[c], x[ib]);
+          copy_after(ib * Tr::NKF + c);
+        }
       }
       interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
       __builtin_amdgcn_s_setprio(0);
@@ -545,7 +568,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int ib = 0; ib < 2; ++ib) {
         x[ib] = zero16();
 #pragma unroll
-        for (int c = 0; c < Tr::NKF; ++c) x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
+        for (int c = 0; c < Tr::NKF; ++c) {
+          x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
+          copy_after(ib * Tr::NKF + c);
+        }
       }
       interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
       __builtin_amdgcn_s_setprio(0);
@@ -585,6 +611,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     qs = qs == 2 ? 0 : qs + 1;
     ds ^= 1;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // Role 1: the dK products of the last tile (its Q is still in LDS: nothing has been stored since).
   if (role == 1 && qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
 

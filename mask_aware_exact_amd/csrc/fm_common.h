@@ -493,6 +493,11 @@ struct TileCopy {
   __device__ __forceinline__ void issue(int k) const {
     lds_copy16(gb, min(off0 + (uint32_t)k * STEP, lim), lds0 + (uint32_t)k * (NW * 1024u));
   }
+  // Instruction k of the same copy for another matrix of the same shape and rows (its own tile base and
+  // LDS address, same lane offsets).
+  __device__ __forceinline__ void issue_to(const char* gb2, uint32_t lds2, int k) const {
+    lds_copy16(gb2, min(off0 + (uint32_t)k * STEP, lim), lds2 + (uint32_t)k * (NW * 1024u));
+  }
 };
 
 // 16-byte global/LDS copy helpers.
