@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       df[c] = typename M::frag{};
     }
   }
-  const float Di = part + __shfl_xor(part, 32, 64);
+  const float Di = pair_sum(part);
   float lse2 = INFINITY;  // rows past N or without any unmasked key: exp(S - lse) = 0
   if (row < Nq) {
     const float l = a.lse[(size_t)bh * Nq + row];

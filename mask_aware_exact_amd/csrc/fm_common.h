@@ -208,6 +208,18 @@ __device__ __forceinline__ float select_neg_inf(int all_ones_if_masked, float x)
   return __uint_as_float((__float_as_uint(x) & ~m) | (0xff800000u & m));
 }
 
+// Max / sum over the lane pair (l, l ^ 32), the same value on both lanes, without an LDS round trip:
+// v_permlane32_swap with both operands x leaves lane (l & 31)'s x in the first result and lane
+// (l & 31) + 32's in the second, on every lane (checked on the MI355X).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ------------------------------------------------------------------ matrix-core traits
 
 template <typename T>

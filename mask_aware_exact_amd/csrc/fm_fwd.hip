@@ -253,7 +253,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
     __builtin_amdgcn_s_setprio(0);
     // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
-    float mx = -INFINITY;
     if (need_mask) {
       tile_column_words(cw_lds[wave], &vec_lds[buf][0][0], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut, lane);
 #pragma unroll
@@ -262,21 +261,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const i32x4 w4 = column_words4(cw_lds[wave], jb, q4, g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = select_neg_inf(row_mask_of(w4[e], l32), s[jb][4 * q4 + e]);
-            s[jb][4 * q4 + e] = x;
-            mx = fmaxf(mx, x);
-          }
+          for (int e = 0; e < 4; ++e) s[jb][4 * q4 + e] = select_neg_inf(row_mask_of(w4[e], l32), s[jb][4 * q4 + e]);
         }
       }
-    } else {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-      }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    }
+    mx = pair_max(mx) * sl2;
     // Raise the reference only when some row of the wave would exceed it by more than the threshold.
     const bool grow = mx > m_ref + RESCALE_THRESHOLD;
     if (__ballot(grow) != 0) {
@@ -325,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // Epilogue: out = O / l, lse = m_ref * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   if (row < Nq) {
     const bool dead = !(l_tot > 0.f);
     const float inv = dead ? 0.f : 1.f / l_tot;
