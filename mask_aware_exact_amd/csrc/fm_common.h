@@ -495,10 +495,15 @@ struct TileCopy {
   uint32_t lim;    // lane: byte offset of the same chunk position in row nrows - 1
   __device__ __forceinline__ void prep(bf16* tile, const bf16* __restrict__ g, int row0, int nrows, int wave,
                                        int lane) {
+    prep_at(lds_addr(tile), g, row0, nrows, wave, lane);
+  }
+  // The same with the tile's LDS byte address given (wave-uniform).
+  __device__ __forceinline__ void prep_at(uint32_t tile_lds, const bf16* __restrict__ g, int row0, int nrows, int wave,
+                                          int lane) {
     const int rl = wave * RPI + lane / CPW;
     const int col = ((lane % CPW) ^ swz_key<D>(rl)) << 4;
     gb = reinterpret_cast<const char*>(g + (size_t)row0 * D);
-    lds0 = lds_addr(tile) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+    lds0 = tile_lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
     off0 = (uint32_t)(rl * RB + col);
     lim = (uint32_t)((nrows - 1 - row0) * RB + col);
   }

@@ -201,6 +201,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   int kt = next_live_tile(win, 0, kt_end, class_of, lane);
   if (kt < kt_end) fetch(kt, 0);
   int buf = 0;
+  // Loop-invariant parts of the next tile's copies: LDS bases of the tile buffers, and this wave's mask
+  // vector (wave w of the first four copies LTS, LTE, UTS, UTE when present).
+  const uint32_t k_lds0 = lds_addr(k_lds), v_lds0 = lds_addr(v_lds), vec_lds0 = lds_addr(vec_lds);
+  const int* vsrc = wv == 0 ? a.lts : wv == 1 ? a.lte : wv == 2 ? a.uts : a.ute;
+  const bool vcopy = vsrc != nullptr;
+  if (vcopy) vsrc += vrow;
 
   while (kt < kt_end) {
     const int c0 = kt * BC;
@@ -208,6 +214,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     stash(buf);
     if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // this tile's direct copies have landed
     __syncthreads();
+    // the first two K fragments, read before the tile scan so that their latency overlaps it
+    bf16x8 kpre[2];
+    if constexpr (SWZ) {
+      kpre[0] = krd.read(reinterpret_cast<const bf16*>(k_lds[buf]), 0, 0);
+      kpre[1] = krd.read(reinterpret_cast<const bf16*>(k_lds[buf]), 0, 1);
+    }
     const int kt_next = next_live_tile(win, kt + 1, kt_end, class_of, lane);
     // bf16: the next tile's copies go out one at a time between the score products below, so that they
     // queue while the matrix cores work instead of holding up the products. Without a next tile the
@@ -215,9 +227,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     TileCopy<D, BC, 4> kcp, vcp;
     if constexpr (SWZ) {
       const int cn = (kt_next < kt_end ? kt_next : kt) * BC;
-      kcp.prep(reinterpret_cast<bf16*>(k_lds[buf ^ 1]), reinterpret_cast<const bf16*>(kg), cn, N, wave, lane);
-      vcp.prep(reinterpret_cast<bf16*>(v_lds[buf ^ 1]), reinterpret_cast<const bf16*>(vg), cn, N, wave, lane);
-      if (kt_next < kt_end) fetch_vectors(kt_next, buf ^ 1);
+      const uint32_t boff = (uint32_t)(buf ^ 1) * (BC * D * 2);
+      kcp.prep_at(k_lds0 + boff, reinterpret_cast<const bf16*>(kg), cn, N, wave, lane);
+      vcp.prep_at(v_lds0 + boff, reinterpret_cast<const bf16*>(vg), cn, N, wave, lane);
+      if (vcopy && kt_next < kt_end)
+        lds_copy4(vsrc, (uint32_t)min(kt_next * BC + lane, N - 1) * 4u,
+                  vec_lds0 + (uint32_t)(buf ^ 1) * (4 * BC * 4) + (uint32_t)wv * (BC * 4));
     } else {
       if (kt_next < kt_end) fetch(kt_next, buf ^ 1);
     }
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         static_assert(NC == Tr::NQF, "one copy per two score products");
 #pragma unroll
         for (int c = 0; c < Tr::NQF; ++c) {
-          s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
+          s[jb] = M::mma(jb == 0 && c < 2 ? kpre[c] : krd.read(kt_lds, jb, c), qf[c], s[jb]);
           if (c & 1) {
             const int k = (jb * Tr::NQF + c) >> 1;
             if (k < NC / 2) kcp.issue(k); else vcp.issue(k - NC / 2);
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int c = 0; c < Tr::NQF; ++c) s[jb] = M::mma(load_kcontig_frag<T>(krow + c * M::KW), qf[c], s[jb]);
       }
     }
-    interleave_reads<2 * Tr::NQF, 2 * Tr::NQF, 2>();
+    interleave_reads<2 * Tr::NQF, 2 * Tr::NQF - 2, 2>();
 
     __builtin_amdgcn_s_setprio(0);
     // Scores stay unscaled until the exponent (scale * log2(e) > 0 keeps the max); masked ones are -inf.
