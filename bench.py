@@ -237,6 +237,34 @@ def time_workload(fm, wl: Workload, steps: int, warmup: int, use_sched: bool = F
     return wall, parts.mean(axis=0), ok
 
 
+def bounds_bytes(B: int, Hm: int, N: int, nvec: int) -> int:
+    """Algorithmic HBM bytes of one fm_tile_bounds call: every vector element read once, 32 bytes of
+    bounds written per 64-column key tile."""
+    return 4 * nvec * B * Hm * N + 32 * B * Hm * ((N + 63) // 64)
+
+
+def time_bounds(fm, B: int, Hm: int, N: int, dev, reps: int = 20):
+    """Mean fm_tile_bounds time (ms, HIP events on the launch stream) on four seeded vectors of
+    [B, Hm, N] with values in [0, N]."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    vecs = [torch.randint(0, N + 1, (B, Hm, N), dtype=torch.int32, device=dev, generator=g) for _ in range(4)]
+    out = torch.empty(fm.fm_bounds_elems(B, Hm, N), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        fm.fm_tile_bounds(*vecs, B, Hm, N, bounds=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fm.fm_tile_bounds(*vecs, B, Hm, N, bounds=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del vecs, out
+    return ms
+
+
 def time_workload_compacted(fm, wl: Workload, steps: int, warmup: int):
     """The same step through key compaction: fm_compact_keys, fm_gather_rows (K, V), fm_tile_bounds,
     fm_fwd and fm_bwd without the causal flag, fm_gather_rows (dK, dV back). All of it is timed."""
@@ -421,6 +449,25 @@ def cpu_baseline(wl: Workload, budget_heads: int, max_tokens: int):
             "seconds": round(dt, 2), "cpu": platform.processor() or platform.machine()}
 
 
+def prepass_record(fm, wl: Workload, bounds_ms: float, dev):
+    """Achieved HBM rate of fm_tile_bounds (HBM-bound): on the workload's own vectors, where a ~1 MiB
+    read leaves it launch-latency bound, and at B*Hm*N = 2^26 (1 GiB of four vectors) to show the
+    bandwidth regime."""
+    nvec = sum(v is not None for v in wl.vecs)
+    rec = {"unit": "GB/s", "peak": PEAK_HBM_GBS}
+    if nvec:
+        b = bounds_bytes(wl.B, wl.spec.Hm, wl.N, nvec)
+        rec["workload"] = {"vectors": nvec, "bytes": b, "ms": round(bounds_ms, 4),
+                           "achieved": round(b / (bounds_ms * 1e-3) / 1e9, 1)}
+    B, Hm, N = 1, 512, 131072  # 2^26 columns
+    ms = time_bounds(fm, B, Hm, N, dev)
+    b = bounds_bytes(B, Hm, N, 4)
+    ach = b / (ms * 1e-3) / 1e9
+    rec["2^26 columns (B=1, Hm=512, N=131072, four vectors)"] = {
+        "bytes": b, "ms": round(ms, 4), "achieved": round(ach, 1), "frac": round(ach / PEAK_HBM_GBS, 4)}
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -498,6 +545,7 @@ def main():
         "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[2] * 1e-3) / 1e12, 2),
                          "fm_bwd": round(bwd_tflops, 2)},
         "finite_outputs": ok,
+        "prepass": prepass_record(fm, wl, float(parts_ms[0]), dev),
         "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_dq_kernel then bwd_dkdv_pair_kernel)",
                      "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(wl.name),
@@ -516,8 +564,9 @@ def main():
     if args.sweep:
         sweep = {}
         for name in WORKLOADS:
-            if name == wl.name or WORKLOADS[name][0] == 1:
+            if name == wl.name:
                 continue
+            print(f"sweep: {name}", file=sys.stderr, flush=True)
             del wl
             torch.cuda.empty_cache()
             wl = Workload(name, dev)
@@ -526,7 +575,7 @@ def main():
             w0, p0, _ = time_workload(fm, wl, n, 1, not use_sched)
             ms = w2 * 1e3 / n
             sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
-                           "U": int(wl.U), "fwd_ms": round(float(p2[2]), 3), "bwd_ms": round(float(p2[3]), 3),
+                           "d": wl.d, "U": int(wl.U), "fwd_ms": round(float(p2[2]), 3), "bwd_ms": round(float(p2[3]), 3),
                            "bounds_ms": round(float(p2[0]), 4),
                            "schedule_ms": round(float(p2[1] if use_sched else p0[1]), 4),
                            "finite": ok2,
@@ -538,6 +587,7 @@ def main():
         # each rank's contiguous 16384 query rows against all keys
         del wl
         torch.cuda.empty_cache()
+        print("sweep: context-parallel rank shares", file=sys.stderr, flush=True)
         wl = Workload("long_context_causal_document", dev)
         ranks = 8
         per = wl.N // ranks
@@ -567,6 +617,7 @@ def main():
             "imbalance_max_over_mean": round(max(ms) / (sum(ms) / len(ms)), 3)}
         del wl
         torch.cuda.empty_cache()
+        print("sweep: key compaction", file=sys.stderr, flush=True)
         wl = Workload("dpo_rm_causal_key_drop", dev)
         n = max(3, args.steps // 4)
         w3, ok3 = time_workload_compacted(fm, wl, n, 1)
@@ -575,6 +626,7 @@ def main():
             "U": int(wl.U), "compactable": ok3}
         # hash-bucket attention, against plain causal attention at the same shape
         for name in W.HASH_WORKLOADS:
+            print(f"sweep: {name}", file=sys.stderr, flush=True)
             del wl
             torch.cuda.empty_cache()
             hw = HashWorkload(name, dev)
