@@ -125,6 +125,32 @@ def test_bounds_and_classes_bit_exact(fm, mask, N):
         assert np.array_equal(cls, OT.tile_classes(ref_b, N, spec.causal, qblock))
 
 
+@pytest.mark.parametrize("N,offset,pairs", [(256, 1, "both"), (1000, 3, "lt"), (4096, 0, "both"),
+                                            (777, 0, "ut"), (64, 2, "both"), (1024, 0, "lt"), (3, 0, "both")])
+def test_bounds_random_vectors_and_offsets(fm, N, offset, pairs):
+    """Bounds of arbitrary vectors (values below 0 and past N included), with rows that start off the
+    16-byte grid (offset elements into the allocation) and N off the multiple of 4, which take the
+    kernel's per-column load path, and with one interval pair missing."""
+    rng = np.random.default_rng(N * 10 + offset)
+    B, Hm = 2, 3
+    vals = [rng.integers(-N, 2 * N + 1, size=(B, Hm, N), dtype=np.int32) for _ in range(4)]
+    if pairs == "lt":
+        vals[2] = vals[3] = None
+    if pairs == "ut":
+        vals[0] = vals[1] = None
+    dev = []
+    for v in vals:
+        if v is None:
+            dev.append(None)
+            continue
+        buf = torch.zeros(B * Hm * N + offset, dtype=torch.int32, device="cuda")
+        view = buf[offset:].view(B, Hm, N)
+        view.copy_(torch.from_numpy(v))
+        dev.append(view)
+    got = fm.fm_tile_bounds(*dev, B, Hm, N).cpu().numpy()
+    assert np.array_equal(got, OT.tile_bounds(tuple(vals), B, Hm, N))
+
+
 def test_api_errors_on_gpu(fm):
     q = torch.zeros(1, 2, 64, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fm.FmError) as e:
