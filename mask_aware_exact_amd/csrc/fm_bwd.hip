@@ -62,7 +62,7 @@ struct DqTraits {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_dq_kernel(BwdArgs a) {
   using Tr = DqTraits<T, D>;
   using M = MM<T>;
   constexpr int BR = Tr::BR, BC = Tr::BC, KP = Tr::KP, VP = Tr::VP, CPR = Tr::CPR, CH = Tr::CH;
