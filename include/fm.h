@@ -76,6 +76,9 @@ size_t fm_bounds_elems(int B, int Hm, int N);
  *   bounds[b][hm][t][0..7] = min LTS, max LTS, min LTE, max LTE, min UTS, max UTS, min UTE, max UTE.
  * A NULL pair writes the canonical empty values: LT -> N, N, N, N; UT -> 0, 0, 0, 0.
  * The pages name no such pass; it is the per-tile summary from which the tile classification is read.
+ * The vectors need no alignment beyond int32; when every row starts on a 16-byte boundary (16-byte
+ * aligned pointers and N a multiple of 4) they are read with 16-byte loads. HBM-bound: each vector
+ * element is read once.
  * Errors: FM_ERR_INVALID (bounds NULL, sizes out of range, half-NULL pair). */
 fm_status fm_tile_bounds(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute,
                          int B, int Hm, int N, int32_t* bounds, hipStream_t stream);
