@@ -96,6 +96,44 @@ def test_causal_flag_equals_vector_causal_bitwise(fm):
     C.compare(gb, C.run_oracle(b), "bf16")
 
 
+@pytest.mark.parametrize("kind", ["scores_x6", "rising_max"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_scores_and_rising_maxima(fm, kind, d):
+    """Scores far outside the N(0, 1) recipe: q scaled by 6 (scores up to ~+-25, log2 units ~+-40), or a
+    query component of 40 against a key component rising from -25 to 25 along the key axis, so that the
+    live 64-key tiles of a row raise its max by 16-21 log2 units each (all but the partly masked diagonal
+    tile) and the forward rescales its accumulator on nearly every tile. Both sides consume the same bf16
+    inputs.
+
+    Bars: lse 1e-3 and dq/dk/dv relative Frobenius 2e-2 as for the workloads. For out, 1e-2 plus half a
+    bf16 ulp of the reference value: with a peaked softmax an output row is close to a single value row,
+    so |out| reaches 4 and more, where the bf16 rounding of the output alone is up to 2^-6."""
+    base = C.make_case(2, "causal_document", 1, 2, 900, d, "bf16")
+    q, k = base.q.float(), base.k.float()
+    if kind == "scores_x6":
+        q = q * 6.0
+    else:
+        q[..., 0] = 40.0
+        k[..., 0] = torch.linspace(-25.0, 25.0, base.N).view(1, 1, base.N)
+    case = C.Case(f"{kind}-d{d}", base.spec, base.B, base.H, base.N, d, "bf16", q.to(torch.bfloat16),
+                  k.to(torch.bfloat16), base.v, base.do)
+    print(f"\ncase {case.name}", flush=True)
+    gpu = C.run_gpu(case, fm)
+    ref = C.run_oracle(case)
+    out_g = gpu["out"].double().numpy()
+    mag = np.maximum(np.abs(ref["out"]), 2.0 ** -126)
+    half_ulp = np.exp2(np.floor(np.log2(mag)) - 8.0)  # bf16: 8 significant bits
+    err = np.abs(out_g - ref["out"])
+    assert np.all(err <= 1e-2 + half_ulp), float(np.max(err - half_ulp))
+    lse_g = gpu["lse"].double().numpy()
+    assert np.array_equal(np.isfinite(lse_g), np.isfinite(ref["lse"]))
+    fin = np.isfinite(ref["lse"])
+    assert np.max(np.abs(lse_g[fin] - ref["lse"][fin]), initial=0.0) <= C.TOL["bf16"]["lse"]
+    for name in ("dq", "dk", "dv"):
+        e = C.rel_fro(gpu[name].double().numpy(), ref[name])
+        assert e <= C.TOL["bf16"]["grad"], (name, e)
+
+
 def test_forward_is_deterministic(fm):
     case = C.make_case(4, "causal_document", 1, 2, 1500, 128, "bf16")
     a, b = C.run_gpu(case, fm), C.run_gpu(case, fm)
