@@ -163,14 +163,17 @@ def test_bounds_and_classes_bit_exact(fm, mask, N):
         assert np.array_equal(cls, OT.tile_classes(ref_b, N, spec.causal, qblock))
 
 
-@pytest.mark.parametrize("N,offset,pairs", [(256, 1, "both"), (1000, 3, "lt"), (4096, 0, "both"),
-                                            (777, 0, "ut"), (64, 2, "both"), (1024, 0, "lt"), (3, 0, "both")])
-def test_bounds_random_vectors_and_offsets(fm, N, offset, pairs):
+@pytest.mark.parametrize("N,offset,pairs,Hm", [(256, 1, "both", 3), (1000, 3, "lt", 3), (4096, 0, "both", 3),
+                                               (777, 0, "ut", 3), (64, 2, "both", 3), (1024, 0, "lt", 3),
+                                               (3, 0, "both", 3), (40000, 0, "both", 32), (40001, 0, "lt", 32)])
+def test_bounds_random_vectors_and_offsets(fm, N, offset, pairs, Hm):
     """Bounds of arbitrary vectors (values below 0 and past N included), with rows that start off the
     16-byte grid (offset elements into the allocation) and N off the multiple of 4, which take the
-    kernel's per-column load path, and with one interval pair missing."""
+    kernel's per-column load path, and with one interval pair missing. The two largest cases have
+    enough 256-column chunks (2 x 32 x 157) for the kernel's two-chunks-per-wave form, on the 16-byte and
+    the per-column load paths."""
     rng = np.random.default_rng(N * 10 + offset)
-    B, Hm = 2, 3
+    B = 2
     vals = [rng.integers(-N, 2 * N + 1, size=(B, Hm, N), dtype=np.int32) for _ in range(4)]
     if pairs == "lt":
         vals[2] = vals[3] = None
