@@ -216,6 +216,27 @@ fm_status fm_bucket_sort(const int32_t* qbucket, const int32_t* kbucket, int B, 
                          int32_t* qpos, int32_t* kidx, int32_t* kpos, int32_t* lts, int32_t* lte, int32_t* uts,
                          int32_t* ute, hipStream_t stream);
 
+/* fm_fwd and fm_bwd on a reordered problem (the sorted one above), with the outputs stored in the
+ * original order directly instead of gathered back (same SCFA passage: the hash attention's results are
+ * the original tokens'). q, k, v, dout and lse are in the reordered order, exactly as for fm_fwd / fm_bwd.
+ *   omap, qmap: int32 [B, H, N], reordered row r -> original row (fm_bucket_sort's qidx);
+ *   kmap:       int32 [B, H, N], reordered key c -> original key (its kidx).
+ *   fm_fwd_mapped writes out[b][h][omap[r]] = row r of the result; lse stays at row r.
+ *   fm_bwd_mapped reads out through qmap (out as fm_fwd_mapped wrote it), writes dq[b][h][qmap[r]] and
+ *   dk, dv [b][h][kmap[c]]. Values equal fm_fwd / fm_bwd followed by the gathers with qpos / kpos, bit for
+ *   bit. A map entry outside [0, N) drops that row: nothing is written for it, and its out row reads as
+ *   zero. With a map that is not a permutation, rows not hit keep their previous contents.
+ * bf16 only. Errors: as fm_fwd / fm_bwd; FM_ERR_INVALID for a NULL map; FM_ERR_UNSUPPORTED for float32. */
+fm_status fm_fwd_mapped(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
+                        const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                        const int32_t* bounds, const int32_t* sched, int causal, float scale, const int32_t* omap,
+                        void* out, float* lse, hipStream_t stream);
+fm_status fm_bwd_mapped(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts,
+                        const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds,
+                        const int32_t* sched, int causal, float scale, const int32_t* qmap, const int32_t* kmap,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Test hook: the tile classifier the kernels use, materialised. For each (b, hm, query tile of
  * qblock rows, key tile of kblock columns), clipped to N, writes classes[b][hm][qt][kt]:
  *   2 FULL    the causal triangle or one interval covers every (row, column) of the tile

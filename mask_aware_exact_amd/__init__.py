@@ -24,7 +24,8 @@ NONE, PARTIAL, FULL = 0, 1, 2
 EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "fm_schedule_elems",
             "fm_tile_schedule", "fm_fwd",
             "fm_bwd_workspace_bytes", "fm_bwd", "fm_fwd_rows", "fm_bwd_rows", "fm_tile_classes",
-            "fm_compact_keys", "fm_gather_rows", "fm_lsh_buckets", "fm_bucket_sort", "fm_status_str")
+            "fm_compact_keys", "fm_gather_rows", "fm_lsh_buckets", "fm_bucket_sort", "fm_fwd_mapped",
+            "fm_bwd_mapped", "fm_status_str")
 
 
 class FmError(RuntimeError):
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P, S, P]
     lib.fm_tile_classes.restype = I
     lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
+    lib.fm_fwd_mapped.restype = I
+    lib.fm_fwd_mapped.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P]
+    lib.fm_bwd_mapped.restype = I
+    lib.fm_bwd_mapped.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P, P, P, S, P]
     lib.fm_fwd_rows.restype = I
     lib.fm_fwd_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P]
     lib.fm_bwd_rows.restype = I
@@ -219,6 +224,49 @@ def fm_bwd(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, boun
     _check(lib.fm_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N, d,
                       *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), int(bool(causal)), float(scale), _ptr(dq),
                       _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)), "fm_bwd")
+    return dq, dk, dv
+
+
+def fm_fwd_mapped(q, k, v, omap, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False, scale=None,
+                  out=None, lse=None, stream=None, sched=None):
+    """fm_fwd on a reordered problem with out stored in the original order: out row omap[b, h, r] receives
+    result row r (omap int32 [B, H, N]); lse stays in the reordered order. bf16 only."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, omap, bounds, sched, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.fm_fwd_mapped(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, N, d, *[_ptr(x) for x in vecs], Hm,
+                             _ptr(bounds), _ptr(sched), int(bool(causal)), float(scale), _ptr(_vec(omap)),
+                             _ptr(out), _ptr(lse), _stream(stream)), "fm_fwd_mapped")
+    return out, lse
+
+
+def fm_bwd_mapped(q, k, v, out, dout, lse, qmap, kmap, lts=None, lte=None, uts=None, ute=None, bounds=None,
+                  causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, sched=None):
+    """fm_bwd on a reordered problem: out (original order, as fm_fwd_mapped wrote it) is read through qmap;
+    dq is stored at rows qmap, dk and dv at rows kmap (int32 [B, H, N] each). bf16 only."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, out, dout, lse, qmap, kmap, bounds, sched, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fm_bwd_workspace_bytes(q.dtype, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fm_bwd_mapped(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N,
+                             d, *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), int(bool(causal)),
+                             float(scale), _ptr(_vec(qmap)), _ptr(_vec(kmap)), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(workspace), workspace.numel(), _stream(stream)), "fm_bwd_mapped")
     return dq, dk, dv
 
 

@@ -15,12 +15,12 @@ hipError_t launch_tile_classes(const int* bounds, int rows, int N, int causal, i
 hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
                       const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
                       int Nq, int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream);
+                      hipStream_t stream, const int* omap);
 hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
                       const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
                       int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream);
+                      hipStream_t stream, const int* qmap, const int* kmap);
 int fwd_qblock();
 hipError_t launch_tile_schedule(const int* bounds, int rows, int Nq, int Nk, int q_off, int causal, int* sched,
                                 hipStream_t stream);
@@ -107,10 +107,11 @@ fm_status fm_tile_schedule(const int32_t* bounds, int B, int Hm, int Nq, int Nk,
   return from_hip(fm::launch_tile_schedule(bounds, B * Hm, Nq, Nk, q_off, causal != 0, sched, stream));
 }
 
-fm_status fm_fwd_rows(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int Nq, int Nk,
-                      int q_off, int d, const int32_t* lts, const int32_t* lte, const int32_t* uts,
-                      const int32_t* ute, int Hm, const int32_t* bounds, const int32_t* sched, int causal,
-                      float scale, void* out, float* lse, hipStream_t stream) {
+namespace {
+fm_status fwd_impl(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int Nq, int Nk,
+                   int q_off, int d, const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute,
+                   int Hm, const int32_t* bounds, const int32_t* sched, int causal, float scale, const int32_t* omap,
+                   void* out, float* lse, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr) return FM_ERR_INVALID;
   if (!rows_ok(B, H, Nq, Nk, q_off) || !std::isfinite(scale) || !(scale > 0.f)) return FM_ERR_INVALID;
   fm_status st = mask_args_ok(lts, lte, uts, ute, Hm, H, bounds);
@@ -119,7 +120,26 @@ fm_status fm_fwd_rows(const void* q, const void* k, const void* v, fm_dtype dtyp
   if (st != FM_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FM_ERR_INVALID;
   return from_hip(fm::launch_fwd(dtype == FM_BF16, d, q, k, v, out, lse, lts, lte, uts, ute, bounds, B, H, Nq, Nk,
-                                 q_off, Hm, sched, causal != 0, scale, stream));
+                                 q_off, Hm, sched, causal != 0, scale, stream, omap));
+}
+}  // namespace
+
+fm_status fm_fwd_rows(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int Nq, int Nk,
+                      int q_off, int d, const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                      const int32_t* ute, int Hm, const int32_t* bounds, const int32_t* sched, int causal,
+                      float scale, void* out, float* lse, hipStream_t stream) {
+  return fwd_impl(q, k, v, dtype, B, H, Nq, Nk, q_off, d, lts, lte, uts, ute, Hm, bounds, sched, causal, scale,
+                  nullptr, out, lse, stream);
+}
+
+fm_status fm_fwd_mapped(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
+                        const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                        const int32_t* bounds, const int32_t* sched, int causal, float scale, const int32_t* omap,
+                        void* out, float* lse, hipStream_t stream) {
+  if (omap == nullptr) return FM_ERR_INVALID;
+  if (dtype != FM_BF16) return FM_ERR_UNSUPPORTED;
+  return fwd_impl(q, k, v, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, sched, causal, scale, omap, out,
+                  lse, stream);
 }
 
 fm_status fm_fwd(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
@@ -136,11 +156,12 @@ size_t fm_bwd_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d) {
   return round_up(rows * sizeof(float));
 }
 
-fm_status fm_bwd_rows(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                      const float* lse, fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d,
-                      const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
-                      const int32_t* bounds, const int32_t* sched, int causal, float scale, void* dq, void* dk,
-                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+fm_status bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                   fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d, const int32_t* lts,
+                   const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds,
+                   const int32_t* sched, int causal, float scale, const int32_t* qmap, const int32_t* kmap,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return FM_ERR_INVALID;
@@ -156,7 +177,28 @@ fm_status fm_bwd_rows(const void* q, const void* k, const void* v, const void* o
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FM_ERR_WORKSPACE;
   float* dd = static_cast<float*>(workspace);
   return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dd, lts, lte, uts, ute,
-                                 bounds, B, H, Nq, Nk, q_off, Hm, sched, causal != 0, scale, stream));
+                                 bounds, B, H, Nq, Nk, q_off, Hm, sched, causal != 0, scale, stream, qmap, kmap));
+}
+}  // namespace
+
+fm_status fm_bwd_rows(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d,
+                      const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
+                      const int32_t* bounds, const int32_t* sched, int causal, float scale, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(q, k, v, out, dout, lse, dtype, B, H, Nq, Nk, q_off, d, lts, lte, uts, ute, Hm, bounds, sched,
+                  causal, scale, nullptr, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+fm_status fm_bwd_mapped(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts,
+                        const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds,
+                        const int32_t* sched, int causal, float scale, const int32_t* qmap, const int32_t* kmap,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (qmap == nullptr || kmap == nullptr) return FM_ERR_INVALID;
+  if (dtype != FM_BF16) return FM_ERR_UNSUPPORTED;
+  return bwd_impl(q, k, v, out, dout, lse, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, sched, causal,
+                  scale, qmap, kmap, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,

@@ -42,6 +42,10 @@ struct BwdArgs {
   int causal;
   float scale;
   float scale_log2;
+  // null, or [B, H, Nq] / [B, H, Nk]: row r of out (read) and dq (written) of (b, h) is row qmap[r]; key
+  // row j of dk and dv (written) is row kmap[j]. Rows outside the range are not written and read as zero.
+  const int* qmap;
+  const int* kmap;
 };
 
 // ------------------------------------------------------------------ 1. dQ (and D), query-tile parallel
@@ -112,13 +116,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
   // Q^T and dO^T operands (k = d) for this lane's row, D_i and lse_i.
   typename M::frag qf[Tr::NQF], df[Tr::NQF];
   float part = 0.f;
+  const int orow = (a.qmap != nullptr && row < Nq) ? a.qmap[(size_t)bh * Nq + row] : row;  // out / dq row
+  const bool orow_ok = (unsigned)orow < (unsigned)Nq;
 #pragma unroll
   for (int c = 0; c < Tr::NQF; ++c) {
     if (row < Nq) {
       const size_t e = (size_t)row * D + c * M::KW + g * M::E;
       qf[c] = load_kcontig_frag<T>(qg + e);
       df[c] = load_kcontig_frag<T>(dog + e);
-      const typename M::frag of = load_kcontig_frag<T>(og + e);
+      const typename M::frag of = orow_ok ? load_kcontig_frag<T>(og + (size_t)orow * D + c * M::KW + g * M::E)
+                                          : typename M::frag{};
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) part += (float)df[c][s] * (float)of[s];
@@ -305,8 +312,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
 
   if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // dq = scale * dQ^T for this lane's row.
-  if (row < Nq) {
-    T* dqg = static_cast<T*>(a.dq) + qhead + (size_t)row * D;
+  if (row < Nq && orow_ok) {
+    T* dqg = static_cast<T*>(a.dq) + qhead + (size_t)orow * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
@@ -616,8 +623,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   if (role == 1 && qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
 
   // dV = dV^T (role 0) or dK = scale * dK^T (role 1) for this lane's key column, all of d.
-  if (j < N) {
-    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + khead + (size_t)j * D;
+  const int jo = (a.kmap != nullptr && j < N) ? a.kmap[(size_t)bh * N + j] : j;  // the row written
+  if (j < N && (unsigned)jo < (unsigned)N) {
+    bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + khead + (size_t)jo * D;
     const float mul = role == 0 ? 1.f : a.scale;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
@@ -793,7 +801,7 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
                       const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
                       int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream) {
+                      hipStream_t stream, const int* qmap, const int* kmap) {
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.dd = dd;
   a.dq = dq; a.dk = dk; a.dv = dv;
@@ -807,6 +815,8 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * LOG2E;
+  a.qmap = qmap;
+  a.kmap = kmap;
   if (bf16_in) return d == 64 ? launch_bwd_t<bf16, 64>(a, stream) : launch_bwd_t<bf16, 128>(a, stream);
   return d == 64 ? launch_bwd_t<float, 64>(a, stream) : launch_bwd_t<float, 128>(a, stream);
 }

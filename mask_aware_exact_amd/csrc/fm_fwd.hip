@@ -47,6 +47,8 @@ struct FwdArgs {
   int sched_stride;  // int32 per (b, hm) row of sched
   int causal;
   float scale_log2;  // scale * log2(e)
+  const int* omap;   // null, or [B, H, Nq]: out row r of (b, h) is stored at row omap[r] (rows outside
+                     // [0, Nq) are not stored); lse stays at row r
 };
 
 template <typename T, int D>
@@ -336,10 +338,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // Epilogue: out = O / l, lse = m_ref * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
   const float l_tot = pair_sum(l_run);
-  if (row < Nq) {
+  const int orow = (a.omap != nullptr && row < Nq) ? a.omap[(size_t)bh * Nq + row] : row;
+  if (row < Nq && (unsigned)orow < (unsigned)Nq) {
     const bool dead = !(l_tot > 0.f);
     const float inv = dead ? 0.f : 1.f / l_tot;
-    T* og = static_cast<T*>(a.out) + qhead + (size_t)row * D;
+    T* og = static_cast<T*>(a.out) + qhead + (size_t)orow * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
@@ -358,8 +361,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (g == 0) a.lse[(size_t)bh * Nq + row] = dead ? -INFINITY : m_ref * LN2 + logf(l_tot);
   }
+  if (row < Nq && g == 0) a.lse[(size_t)bh * Nq + row] = !(l_tot > 0.f) ? -INFINITY : m_ref * LN2 + logf(l_tot);
 }
 
 template <typename T, int D>
@@ -374,7 +377,7 @@ int fwd_qblock() { return 128; }
 hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
                       const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
                       int Nq, int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream) {
+                      hipStream_t stream, const int* omap) {
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
   a.lts = lts; a.lte = lte; a.uts = uts; a.ute = ute; a.bounds = bounds;
@@ -386,6 +389,7 @@ hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const v
   a.sched_stride = 2 * (a.nq + (Nk + SCHED_UNIT - 1) / SCHED_UNIT);
   a.causal = causal;
   a.scale_log2 = scale * LOG2E;
+  a.omap = omap;
   if (bf16_in) return d == 64 ? launch_fwd_t<bf16, 64>(a, stream) : launch_fwd_t<bf16, 128>(a, stream);
   return d == 64 ? launch_fwd_t<float, 64>(a, stream) : launch_fwd_t<float, 128>(a, stream);
 }

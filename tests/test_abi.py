@@ -111,6 +111,30 @@ def test_bwd_validation(lib):
     assert _bwd(lib, dk=P(0x200008)) == fm.FM_ERR_INVALID
 
 
+def test_mapped_validation(lib):
+    """fm_fwd_mapped / fm_bwd_mapped: the fm_fwd / fm_bwd checks, plus NULL maps and float32 refused."""
+    M = P(0x400000)
+
+    def fwdm(omap=M, dtype=fm.FM_BF16, B=1, q=A, scale=0.125):
+        return lib.fm_fwd_mapped(q, A, A, dtype, B, 2, 100, 64, None, None, None, None, 1, None, None, 0, scale,
+                                 omap, B_, B_, None)
+
+    def bwdm(qmap=M, kmap=M, dtype=fm.FM_BF16, ws_bytes=1 << 30, dq=B_):
+        return lib.fm_bwd_mapped(A, A, A, A, A, A, dtype, 1, 2, 100, 64, None, None, None, None, 1, None, None, 0,
+                                 0.125, qmap, kmap, dq, B_, B_, P(0x300000), ws_bytes, None)
+
+    assert fwdm(omap=None) == fm.FM_ERR_INVALID
+    assert fwdm(dtype=fm.FM_F32) == fm.FM_ERR_UNSUPPORTED
+    assert fwdm(B=0) == fm.FM_ERR_INVALID
+    assert fwdm(q=None) == fm.FM_ERR_INVALID
+    assert fwdm(scale=-1.0) == fm.FM_ERR_INVALID
+    assert bwdm(qmap=None) == fm.FM_ERR_INVALID
+    assert bwdm(kmap=None) == fm.FM_ERR_INVALID
+    assert bwdm(dtype=fm.FM_F32) == fm.FM_ERR_UNSUPPORTED
+    assert bwdm(dq=None) == fm.FM_ERR_INVALID
+    assert bwdm(ws_bytes=16) == fm.FM_ERR_WORKSPACE
+
+
 def test_bounds_and_classes_validation(lib):
     assert lib.fm_tile_bounds(A, A, None, None, 1, 1, 10, None, None) == fm.FM_ERR_INVALID
     assert lib.fm_tile_bounds(A, None, None, None, 1, 1, 10, B_, None) == fm.FM_ERR_INVALID

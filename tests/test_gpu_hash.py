@@ -232,3 +232,29 @@ def test_hash_pipeline_graph_replays(fm):
         junk = (q.float() * 2).sum()  # eager work between replays
         torch.cuda.synchronize()
         del junk
+
+
+@pytest.mark.parametrize("d,nb,drop", [(128, 8, 0.0), (64, 16, 0.1), (128, 3, 0.05)])
+def test_mapped_outputs_equal_gathered(fm, d, nb, drop):
+    """fm_fwd_mapped / fm_bwd_mapped store out, dq, dk, dv straight into the original order: bitwise equal to
+    fm_fwd / fm_bwd on the reordered problem followed by the gathers back, and lse equal in sorted order."""
+    print(f"\nmapped d{d} nb{nb} drop{drop}", flush=True)
+    B, H, N = 2, 3, 1000
+    q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in W.make_tensors(2, 200 + d, B, H, N, d))
+    qb, kb = (torch.from_numpy(x).cuda() for x in W.make_buckets(2, 200 + nb, B, H, N, nb, drop))
+    scale = d ** -0.5
+    qidx, qpos, kidx, kpos, vecs = fm.fm_bucket_sort(qb, kb, nb)
+    qs, dos = fm.fm_gather_rows(q, qidx), fm.fm_gather_rows(do, qidx)
+    ks, vs = fm.fm_gather_rows(k, kidx), fm.fm_gather_rows(v, kidx)
+    bounds = fm.fm_tile_bounds(*vecs, B, H, N)
+    outs, lse = fm.fm_fwd(qs, ks, vs, *vecs, bounds=bounds, causal=False, scale=scale)
+    dqs, dks, dvs = fm.fm_bwd(qs, ks, vs, outs, dos, lse, *vecs, bounds=bounds, causal=False, scale=scale)
+    ref = {"out": fm.fm_gather_rows(outs, qpos), "dq": fm.fm_gather_rows(dqs, qpos),
+           "dk": fm.fm_gather_rows(dks, kpos), "dv": fm.fm_gather_rows(dvs, kpos)}
+    out_m, lse_m = fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=bounds, causal=False, scale=scale)
+    dq_m, dk_m, dv_m = fm.fm_bwd_mapped(qs, ks, vs, out_m, dos, lse_m, qidx, kidx, *vecs, bounds=bounds,
+                                        causal=False, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(lse_m, lse)
+    for name, got in (("out", out_m), ("dq", dq_m), ("dk", dk_m), ("dv", dv_m)):
+        assert torch.equal(got, ref[name]), name
