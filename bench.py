@@ -352,18 +352,16 @@ class HashWorkload:
 
 def time_hash_workload(fm, wl: HashWorkload, steps: int, warmup: int, graph: bool = False):
     """One step: fm_lsh_buckets of Q and K, fm_bucket_sort, fm_gather_rows of Q, K, V, dO into bucket
-    order, fm_tile_bounds, fm_fwd and fm_bwd (no causal flag), fm_gather_rows of out, dq, dk, dv back.
-    All of it is timed. U is counted afterwards from the reordered problem's vectors. With `graph`
-    the 16 launches of a step are captured once in a HIP graph and the timed steps are graph replays (the
-    library allocates nothing and issues no memset, so the step replays as captured); on this stack the
-    replays measured slower than the eager launches, which already run back to back, so eager is the
-    default."""
+    order, fm_tile_bounds, then fm_fwd_mapped and fm_bwd_mapped (no causal flag), which store out, dq, dk
+    and dv straight into the original token order. All of it is timed. U is counted afterwards from the
+    reordered problem's vectors. With `graph` the 12 launches of a step are captured once in a HIP graph
+    and the timed steps are graph replays (the library allocates nothing and issues no memset, so the
+    step replays as captured); the eager step is the workload's rate and the replay time is reported
+    beside it."""
     import torch
     B, H, N = wl.B, wl.H, wl.N
     qs, ks, vs, dos = (torch.empty_like(x) for x in (wl.q, wl.k, wl.v, wl.do))
-    outs = torch.empty_like(wl.q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=wl.q.device)
-    dqs, dks, dvs = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
     out, dq, dk, dv = (torch.empty_like(x) for x in (wl.q, wl.q, wl.k, wl.v))
     ws = torch.empty(fm.fm_bwd_workspace_bytes(torch.bfloat16, B, H, N, wl.d), dtype=torch.uint8,
                      device=wl.q.device)
@@ -380,13 +378,9 @@ def time_hash_workload(fm, wl: HashWorkload, steps: int, warmup: int, graph: boo
         fm.fm_gather_rows(wl.k, kidx, y=ks)
         fm.fm_gather_rows(wl.v, kidx, y=vs)
         b = fm.fm_tile_bounds(*vecs, B, H, N, bounds=bounds)
-        fm.fm_fwd(qs, ks, vs, *vecs, bounds=b, causal=False, scale=wl.scale, out=outs, lse=lse)
-        fm.fm_bwd(qs, ks, vs, outs, dos, lse, *vecs, bounds=b, causal=False, scale=wl.scale, dq=dqs, dk=dks,
-                  dv=dvs, workspace=ws)
-        fm.fm_gather_rows(outs, qpos, y=out)
-        fm.fm_gather_rows(dqs, qpos, y=dq)
-        fm.fm_gather_rows(dks, kpos, y=dk)
-        fm.fm_gather_rows(dvs, kpos, y=dv)
+        fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=b, causal=False, scale=wl.scale, out=out, lse=lse)
+        fm.fm_bwd_mapped(qs, ks, vs, out, dos, lse, qidx, kidx, *vecs, bounds=b, causal=False, scale=wl.scale,
+                         dq=dq, dk=dk, dv=dv, workspace=ws)
         return vecs
 
     for _ in range(warmup):
