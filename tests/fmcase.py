@@ -136,10 +136,12 @@ def run_gpu_compacted(case: Case, fm, dev="cuda"):
     return {k_: ([x.cpu() for x in t] if isinstance(t, list) else t.cpu()) for k_, t in res.items()}
 
 
-def run_gpu_hash(fm, q, k, v, do, qb, kb, nb: int, scale: float):
+def run_gpu_hash(fm, q, k, v, do, qb, kb, nb: int, scale: float, mapped: bool = False):
     """Hash-bucket attention through the C ABI on device tensors: fm_bucket_sort, fm_gather_rows of Q, dO
     (by qidx) and K, V (by kidx), fm_tile_bounds, fm_fwd / fm_bwd without the causal flag on the sorted
     problem, then fm_gather_rows of out, dq (by qpos) and dk, dv (by kpos) back to the original order.
+    With `mapped` the attention runs as fm_fwd_mapped / fm_bwd_mapped (bf16), which store out, dq, dk, dv
+    straight into the original order through qidx and kidx, as the benchmark's hash step does.
     lse stays in sorted order in the library; it is put back in original order here, on the host side
     of the comparison. Returns CPU tensors."""
     B, H, N, d = q.shape
@@ -147,10 +149,16 @@ def run_gpu_hash(fm, q, k, v, do, qb, kb, nb: int, scale: float):
     qs, dos = fm.fm_gather_rows(q, qidx), fm.fm_gather_rows(do, qidx)
     ks, vs = fm.fm_gather_rows(k, kidx), fm.fm_gather_rows(v, kidx)
     bounds = fm.fm_tile_bounds(*vecs, B, H, N)
-    outs, lse_s = fm.fm_fwd(qs, ks, vs, *vecs, bounds=bounds, causal=False, scale=scale)
-    dqs, dks, dvs = fm.fm_bwd(qs, ks, vs, outs, dos, lse_s, *vecs, bounds=bounds, causal=False, scale=scale)
-    out, dq = fm.fm_gather_rows(outs, qpos), fm.fm_gather_rows(dqs, qpos)
-    dk, dv = fm.fm_gather_rows(dks, kpos), fm.fm_gather_rows(dvs, kpos)
+    if mapped:
+        out, lse_s = fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=bounds, causal=False, scale=scale)
+        dq, dk, dv = fm.fm_bwd_mapped(qs, ks, vs, out, dos, lse_s, qidx, kidx, *vecs, bounds=bounds,
+                                      causal=False, scale=scale)
+    else:
+        outs, lse_s = fm.fm_fwd(qs, ks, vs, *vecs, bounds=bounds, causal=False, scale=scale)
+        dqs, dks, dvs = fm.fm_bwd(qs, ks, vs, outs, dos, lse_s, *vecs, bounds=bounds, causal=False,
+                                  scale=scale)
+        out, dq = fm.fm_gather_rows(outs, qpos), fm.fm_gather_rows(dqs, qpos)
+        dk, dv = fm.fm_gather_rows(dks, kpos), fm.fm_gather_rows(dvs, kpos)
     torch.cuda.synchronize()
     lse = torch.gather(lse_s.cpu(), 2, qpos.cpu().long())
     res = {"out": out, "dq": dq, "dk": dk, "dv": dv, "qidx": qidx, "qpos": qpos, "kidx": kidx, "kpos": kpos}

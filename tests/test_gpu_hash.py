@@ -121,8 +121,13 @@ def test_hash_attention_parity(fm, dtype, d, B, H, N, nb, drop):
     gpu = C.run_gpu_hash(fm, q.cuda(), k.cuda(), v.cuda(), do.cuda(), torch.from_numpy(qb).cuda(),
                          torch.from_numpy(kb).cuda(), nb, scale)
     out, lse, dq, dk, dv = OH.hash_attention(C.f64(q), C.f64(k), C.f64(v), C.f64(do), qb, kb, nb, scale)
-    errs = C.compare(gpu, {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, dtype)
+    ref = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    errs = C.compare(gpu, ref, dtype)
     print(f"  {errs}", flush=True)
+    if dtype == "bf16":
+        gm = C.run_gpu_hash(fm, q.cuda(), k.cuda(), v.cuda(), do.cuda(), torch.from_numpy(qb).cuda(),
+                            torch.from_numpy(kb).cuda(), nb, scale, mapped=True)
+        print(f"  mapped {C.compare(gm, ref, dtype)}", flush=True)
 
 
 def test_hash_end_to_end_with_lsh(fm):
@@ -164,7 +169,7 @@ def test_hash_fullsize_sampled(fm, name):
     qb, kb = W.make_buckets(cfg_i, W.HASH_MASK_INDEX, B, H, N, nb, 0.0)
     scale = d ** -0.5
     gpu = C.run_gpu_hash(fm, qd, kd, v.cuda(), do.cuda(), torch.from_numpy(qb).cuda(),
-                         torch.from_numpy(kb).cuda(), nb, scale)
+                         torch.from_numpy(kb).cuda(), nb, scale, mapped=True)
     del qd, kd
     torch.cuda.empty_cache()
     tol = C.TOL["bf16"]
@@ -192,9 +197,10 @@ def test_hash_fullsize_sampled(fm, name):
 
 
 def test_hash_pipeline_graph_replays(fm):
-    """The whole hash pipeline captured in a HIP graph (torch.cuda.CUDAGraph; the library allocates nothing
-    and issues no memset): every replay, with eager work and synchronisations between replays, equals the
-    eager run bitwise (the pipeline has no atomics)."""
+    """The whole hash pipeline, with the gathers back and with the mapped entry points, captured in a HIP
+    graph (torch.cuda.CUDAGraph; the library allocates nothing and issues no memset): every replay, with
+    eager work and synchronisations between replays, equals the eager run bitwise (the pipeline has no
+    atomics)."""
     print("\nhash pipeline graph replays", flush=True)
     B, H, N, d, nb = 1, 2, 1500, 128, 8
     q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in W.make_tensors(2, 103, B, H, N, d))
@@ -210,8 +216,11 @@ def test_hash_pipeline_graph_replays(fm):
         bounds = fm.fm_tile_bounds(*vecs, B, H, N)
         outs, lse = fm.fm_fwd(qs, ks, vs, *vecs, bounds=bounds, causal=False, scale=scale)
         dqs, dks, dvs = fm.fm_bwd(qs, ks, vs, outs, dos, lse, *vecs, bounds=bounds, causal=False, scale=scale)
+        out_m, lse_m = fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=bounds, causal=False, scale=scale)
+        dq_m, dk_m, dv_m = fm.fm_bwd_mapped(qs, ks, vs, out_m, dos, lse_m, qidx, kidx, *vecs, bounds=bounds,
+                                            causal=False, scale=scale)
         return [fm.fm_gather_rows(outs, qpos), fm.fm_gather_rows(dqs, qpos), fm.fm_gather_rows(dks, kpos),
-                fm.fm_gather_rows(dvs, kpos), lse, qb, kb]
+                fm.fm_gather_rows(dvs, kpos), lse, qb, kb, out_m, lse_m, dq_m, dk_m, dv_m]
 
     eager = [t.clone() for t in step()]
     torch.cuda.synchronize()
