@@ -224,8 +224,10 @@ fm_status fm_bucket_sort(const int32_t* qbucket, const int32_t* kbucket, int B, 
  *   fm_fwd_mapped writes out[b][h][omap[r]] = row r of the result; lse stays at row r.
  *   fm_bwd_mapped reads out through qmap (out as fm_fwd_mapped wrote it), writes dq[b][h][qmap[r]] and
  *   dk, dv [b][h][kmap[c]]. Values equal fm_fwd / fm_bwd followed by the gathers with qpos / kpos, bit for
- *   bit. A map entry outside [0, N) drops that row: nothing is written for it, and its out row reads as
- *   zero. With a map that is not a permutation, rows not hit keep their previous contents.
+ *   bit. A map entry outside [0, N) drops that row: nothing is written for it, and the backward reads
+ *   its out row as zero, so that query still adds to dk and dv with a zero row term D. With a map that is
+ *   not a permutation, rows not hit keep their previous contents, and two entries naming the same row
+ *   race (which of the two values remains is unspecified). out, dq, dk, dv must not overlap the inputs.
  * bf16 only. Errors: as fm_fwd / fm_bwd; FM_ERR_INVALID for a NULL map; FM_ERR_UNSUPPORTED for float32. */
 fm_status fm_fwd_mapped(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
                         const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
