@@ -246,7 +246,8 @@ def test_hash_pipeline_graph_replays(fm):
 @pytest.mark.parametrize("d,nb,drop", [(128, 8, 0.0), (64, 16, 0.1), (128, 3, 0.05)])
 def test_mapped_outputs_equal_gathered(fm, d, nb, drop):
     """fm_fwd_mapped / fm_bwd_mapped store out, dq, dk, dv straight into the original order: bitwise equal to
-    fm_fwd / fm_bwd on the reordered problem followed by the gathers back, and lse equal in sorted order."""
+    fm_fwd / fm_bwd on the reordered problem followed by the gathers back, and lse equal in sorted order;
+    the same with the longest-first dispatch schedule."""
     print(f"\nmapped d{d} nb{nb} drop{drop}", flush=True)
     B, H, N = 2, 3, 1000
     q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in W.make_tensors(2, 200 + d, B, H, N, d))
@@ -263,7 +264,13 @@ def test_mapped_outputs_equal_gathered(fm, d, nb, drop):
     out_m, lse_m = fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=bounds, causal=False, scale=scale)
     dq_m, dk_m, dv_m = fm.fm_bwd_mapped(qs, ks, vs, out_m, dos, lse_m, qidx, kidx, *vecs, bounds=bounds,
                                         causal=False, scale=scale)
+    # a dispatch schedule changes only the order of the work units, never a result
+    sched = fm.fm_tile_schedule(bounds, B, H, N, N, False, device=q.device)
+    out_s, lse_s = fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=bounds, sched=sched, causal=False, scale=scale)
+    dq_s, dk_s, dv_s = fm.fm_bwd_mapped(qs, ks, vs, out_s, dos, lse_s, qidx, kidx, *vecs, bounds=bounds,
+                                        sched=sched, causal=False, scale=scale)
     torch.cuda.synchronize()
-    assert torch.equal(lse_m, lse)
-    for name, got in (("out", out_m), ("dq", dq_m), ("dk", dk_m), ("dv", dv_m)):
+    assert torch.equal(lse_m, lse) and torch.equal(lse_s, lse)
+    for name, got, got_s in (("out", out_m, out_s), ("dq", dq_m, dq_s), ("dk", dk_m, dk_s), ("dv", dv_m, dv_s)):
         assert torch.equal(got, ref[name]), name
+        assert torch.equal(got_s, ref[name]), name + " (scheduled)"
