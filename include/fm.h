@@ -228,7 +228,7 @@ fm_status fm_bucket_sort(const int32_t* qbucket, const int32_t* kbucket, int B, 
  *   its out row as zero, so that query still adds to dk and dv with a zero row term D. With a map that is
  *   not a permutation, rows not hit keep their previous contents, and two entries naming the same row
  *   race (which of the two values remains is unspecified). out, dq, dk, dv must not overlap the inputs.
- * bf16 only. Errors: as fm_fwd / fm_bwd; FM_ERR_INVALID for a NULL map; FM_ERR_UNSUPPORTED for float32. */
+ * bf16 and float32, as fm_fwd / fm_bwd. Errors: as fm_fwd / fm_bwd; FM_ERR_INVALID for a NULL map. */
 fm_status fm_fwd_mapped(const void* q, const void* k, const void* v, fm_dtype dtype, int B, int H, int N, int d,
                         const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm,
                         const int32_t* bounds, const int32_t* sched, int causal, float scale, const int32_t* omap,

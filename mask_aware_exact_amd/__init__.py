@@ -230,7 +230,7 @@ def fm_bwd(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, boun
 def fm_fwd_mapped(q, k, v, omap, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False, scale=None,
                   out=None, lse=None, stream=None, sched=None):
     """fm_fwd on a reordered problem with out stored in the original order: out row omap[b, h, r] receives
-    result row r (omap int32 [B, H, N]); lse stays in the reordered order. bf16 only."""
+    result row r (omap int32 [B, H, N]); lse stays in the reordered order."""
     lib = load_library()
     B, H, N, d = q.shape
     vecs = [_vec(x) for x in (lts, lte, uts, ute)]
@@ -249,7 +249,7 @@ def fm_fwd_mapped(q, k, v, omap, lts=None, lte=None, uts=None, ute=None, bounds=
 def fm_bwd_mapped(q, k, v, out, dout, lse, qmap, kmap, lts=None, lte=None, uts=None, ute=None, bounds=None,
                   causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, sched=None):
     """fm_bwd on a reordered problem: out (original order, as fm_fwd_mapped wrote it) is read through qmap;
-    dq is stored at rows qmap, dk and dv at rows kmap (int32 [B, H, N] each). bf16 only."""
+    dq is stored at rows qmap, dk and dv at rows kmap (int32 [B, H, N] each)."""
     lib = load_library()
     B, H, N, d = q.shape
     vecs = [_vec(x) for x in (lts, lte, uts, ute)]

@@ -137,7 +137,6 @@ fm_status fm_fwd_mapped(const void* q, const void* k, const void* v, fm_dtype dt
                         const int32_t* bounds, const int32_t* sched, int causal, float scale, const int32_t* omap,
                         void* out, float* lse, hipStream_t stream) {
   if (omap == nullptr) return FM_ERR_INVALID;
-  if (dtype != FM_BF16) return FM_ERR_UNSUPPORTED;
   return fwd_impl(q, k, v, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, sched, causal, scale, omap, out,
                   lse, stream);
 }
@@ -196,7 +195,6 @@ fm_status fm_bwd_mapped(const void* q, const void* k, const void* v, const void*
                         const int32_t* sched, int causal, float scale, const int32_t* qmap, const int32_t* kmap,
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (qmap == nullptr || kmap == nullptr) return FM_ERR_INVALID;
-  if (dtype != FM_BF16) return FM_ERR_UNSUPPORTED;
   return bwd_impl(q, k, v, out, dout, lse, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, sched, causal,
                   scale, qmap, kmap, dq, dk, dv, workspace, workspace_bytes, stream);
 }

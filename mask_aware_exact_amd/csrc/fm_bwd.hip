@@ -759,9 +759,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
       }
     }
   }
-  if (j < N) {
-    float* dkg = static_cast<float*>(a.dk) + khead + (size_t)j * D;
-    float* dvg = static_cast<float*>(a.dv) + khead + (size_t)j * D;
+  const int jo = (a.kmap != nullptr && j < N) ? a.kmap[(size_t)bh * N + j] : j;  // the row written
+  if (j < N && (unsigned)jo < (unsigned)N) {
+    float* dkg = static_cast<float*>(a.dk) + khead + (size_t)jo * D;
+    float* dvg = static_cast<float*>(a.dv) + khead + (size_t)jo * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll

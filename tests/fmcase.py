@@ -140,7 +140,7 @@ def run_gpu_hash(fm, q, k, v, do, qb, kb, nb: int, scale: float, mapped: bool = 
     """Hash-bucket attention through the C ABI on device tensors: fm_bucket_sort, fm_gather_rows of Q, dO
     (by qidx) and K, V (by kidx), fm_tile_bounds, fm_fwd / fm_bwd without the causal flag on the sorted
     problem, then fm_gather_rows of out, dq (by qpos) and dk, dv (by kpos) back to the original order.
-    With `mapped` the attention runs as fm_fwd_mapped / fm_bwd_mapped (bf16), which store out, dq, dk, dv
+    With `mapped` the attention runs as fm_fwd_mapped / fm_bwd_mapped, which store out, dq, dk, dv
     straight into the original order through qidx and kidx, as the benchmark's hash step does.
     lse stays in sorted order in the library; it is put back in original order here, on the host side
     of the comparison. Returns CPU tensors."""

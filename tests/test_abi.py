@@ -112,7 +112,7 @@ def test_bwd_validation(lib):
 
 
 def test_mapped_validation(lib):
-    """fm_fwd_mapped / fm_bwd_mapped: the fm_fwd / fm_bwd checks, plus NULL maps and float32 refused."""
+    """fm_fwd_mapped / fm_bwd_mapped: the fm_fwd / fm_bwd checks (an unknown dtype refused), plus NULL maps."""
     M = P(0x400000)
 
     def fwdm(omap=M, dtype=fm.FM_BF16, B=1, q=A, scale=0.125):
@@ -124,13 +124,13 @@ def test_mapped_validation(lib):
                                  0.125, qmap, kmap, dq, B_, B_, P(0x300000), ws_bytes, None)
 
     assert fwdm(omap=None) == fm.FM_ERR_INVALID
-    assert fwdm(dtype=fm.FM_F32) == fm.FM_ERR_UNSUPPORTED
+    assert fwdm(dtype=7) == fm.FM_ERR_UNSUPPORTED
     assert fwdm(B=0) == fm.FM_ERR_INVALID
     assert fwdm(q=None) == fm.FM_ERR_INVALID
     assert fwdm(scale=-1.0) == fm.FM_ERR_INVALID
     assert bwdm(qmap=None) == fm.FM_ERR_INVALID
     assert bwdm(kmap=None) == fm.FM_ERR_INVALID
-    assert bwdm(dtype=fm.FM_F32) == fm.FM_ERR_UNSUPPORTED
+    assert bwdm(dtype=7) == fm.FM_ERR_UNSUPPORTED
     assert bwdm(dq=None) == fm.FM_ERR_INVALID
     assert bwdm(ws_bytes=16) == fm.FM_ERR_WORKSPACE
 

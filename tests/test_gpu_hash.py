@@ -124,10 +124,10 @@ def test_hash_attention_parity(fm, dtype, d, B, H, N, nb, drop):
     ref = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
     errs = C.compare(gpu, ref, dtype)
     print(f"  {errs}", flush=True)
-    if dtype == "bf16":
-        gm = C.run_gpu_hash(fm, q.cuda(), k.cuda(), v.cuda(), do.cuda(), torch.from_numpy(qb).cuda(),
-                            torch.from_numpy(kb).cuda(), nb, scale, mapped=True)
-        print(f"  mapped {C.compare(gm, ref, dtype)}", flush=True)
+    # the same through the mapped entry points
+    gm = C.run_gpu_hash(fm, q.cuda(), k.cuda(), v.cuda(), do.cuda(), torch.from_numpy(qb).cuda(),
+                        torch.from_numpy(kb).cuda(), nb, scale, mapped=True)
+    print(f"  mapped {C.compare(gm, ref, dtype)}", flush=True)
 
 
 def test_hash_end_to_end_with_lsh(fm):
@@ -243,14 +243,15 @@ def test_hash_pipeline_graph_replays(fm):
         del junk
 
 
-@pytest.mark.parametrize("d,nb,drop", [(128, 8, 0.0), (64, 16, 0.1), (128, 3, 0.05)])
-def test_mapped_outputs_equal_gathered(fm, d, nb, drop):
+@pytest.mark.parametrize("dtype,d,nb,drop", [("bf16", 128, 8, 0.0), ("bf16", 64, 16, 0.1), ("bf16", 128, 3, 0.05),
+                                              ("f32", 64, 5, 0.1), ("f32", 128, 8, 0.0)])
+def test_mapped_outputs_equal_gathered(fm, dtype, d, nb, drop):
     """fm_fwd_mapped / fm_bwd_mapped store out, dq, dk, dv straight into the original order: bitwise equal to
     fm_fwd / fm_bwd on the reordered problem followed by the gathers back, and lse equal in sorted order;
     the same with the longest-first dispatch schedule."""
-    print(f"\nmapped d{d} nb{nb} drop{drop}", flush=True)
+    print(f"\nmapped {dtype} d{d} nb{nb} drop{drop}", flush=True)
     B, H, N = 2, 3, 1000
-    q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in W.make_tensors(2, 200 + d, B, H, N, d))
+    q, k, v, do = (torch.from_numpy(x).to(C.TORCH_DT[dtype]).cuda() for x in W.make_tensors(2, 200 + d, B, H, N, d))
     qb, kb = (torch.from_numpy(x).cuda() for x in W.make_buckets(2, 200 + nb, B, H, N, nb, drop))
     scale = d ** -0.5
     qidx, qpos, kidx, kpos, vecs = fm.fm_bucket_sort(qb, kb, nb)
