@@ -275,3 +275,44 @@ def test_mapped_outputs_equal_gathered(fm, dtype, d, nb, drop):
     for name, got, got_s in (("out", out_m, out_s), ("dq", dq_m, dq_s), ("dk", dk_m, dk_s), ("dv", dv_m, dv_s)):
         assert torch.equal(got, ref[name]), name
         assert torch.equal(got_s, ref[name]), name + " (scheduled)"
+
+
+def test_mapped_out_of_range_entries_write_nothing(fm):
+    """A map entry outside [0, N) drops its row: the original rows it would have named keep their previous
+    contents, and every other row equals the run with the full permutation."""
+    print("\nmapped out-of-range entries", flush=True)
+    B, H, N, d, nb = 1, 2, 700, 128, 4
+    q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in W.make_tensors(2, 301, B, H, N, d))
+    qb, kb = (torch.from_numpy(x).cuda() for x in W.make_buckets(2, 301, B, H, N, nb, 0.0))
+    qidx, qpos, kidx, kpos, vecs = fm.fm_bucket_sort(qb, kb, nb)
+    qs, dos = fm.fm_gather_rows(q, qidx), fm.fm_gather_rows(do, qidx)
+    ks, vs = fm.fm_gather_rows(k, kidx), fm.fm_gather_rows(v, kidx)
+    bounds = fm.fm_tile_bounds(*vecs, B, H, N)
+    out, lse = fm.fm_fwd_mapped(qs, ks, vs, qidx, *vecs, bounds=bounds, causal=False)
+    dq, dk, dv = fm.fm_bwd_mapped(qs, ks, vs, out, dos, lse, qidx, kidx, *vecs, bounds=bounds, causal=False)
+    rng = np.random.default_rng(5)
+    drop_q = torch.from_numpy(rng.random((B, H, N)) < 0.2).cuda()
+    drop_k = torch.from_numpy(rng.random((B, H, N)) < 0.2).cuda()
+    qmap = torch.where(drop_q, torch.full_like(qidx, -1), qidx)
+    qmap = torch.where(drop_q & (torch.arange(N, device="cuda") % 2 == 0), torch.full_like(qidx, N + 7), qmap)
+    kmap = torch.where(drop_k, torch.full_like(kidx, -3), kidx)
+    sentinel = torch.full_like(out, 7.0)
+    out2, lse2 = fm.fm_fwd_mapped(qs, ks, vs, qmap, *vecs, bounds=bounds, causal=False, out=sentinel.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(lse2, lse)
+    # original rows named only by dropped entries keep the sentinel; the others equal the full run
+    hit_q = torch.zeros((B, H, N + 1), dtype=torch.bool, device="cuda")  # column N collects the dropped entries
+    hit_q.scatter_(2, torch.where(drop_q, torch.full_like(qidx, N), qidx).long(), True)
+    hit_q = hit_q[..., :N]
+    assert torch.equal(out2[hit_q], out[hit_q]) and torch.all(out2[~hit_q] == 7.0)
+    # the backward with the full qmap (out as the full forward wrote it) and a kmap with dropped entries
+    dq2, dk2, dv2 = fm.fm_bwd_mapped(qs, ks, vs, out, dos, lse, qidx, kmap, *vecs, bounds=bounds, causal=False,
+                                     dq=torch.full_like(dq, 7.0), dk=torch.full_like(dk, 7.0),
+                                     dv=torch.full_like(dv, 7.0))
+    torch.cuda.synchronize()
+    hit_k = torch.zeros((B, H, N + 1), dtype=torch.bool, device="cuda")
+    hit_k.scatter_(2, torch.where(drop_k, torch.full_like(kidx, N), kidx).long(), True)
+    hit_k = hit_k[..., :N]
+    assert torch.equal(dq2, dq)
+    assert torch.equal(dk2[hit_k], dk[hit_k]) and torch.all(dk2[~hit_k] == 7.0)
+    assert torch.equal(dv2[hit_k], dv[hit_k]) and torch.all(dv2[~hit_k] == 7.0)
