@@ -132,6 +132,42 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
                  const int32_t* bounds, const int32_t* sched, int causal, float scale, void* dq, void* dk,
                  void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Backward with stored dS tiles: the same gradients as fm_bwd, with dq formed from dS tiles that the
+ * key-tile-parallel pass writes to the workspace instead of by a second pass that recomputes S, dP and dS
+ * (4 d FLOP per unmasked pair less matrix work, for 2 bytes of HBM writes and reads per stored pair).
+ * The pages do not describe the backward's work split; the tiles the mask covers completely are skipped
+ * as in the forward (FlashMask abstract, papers.pytorch.kr 2410.01359). A stored tile is 64 query rows x
+ * 128 keys of bf16 (fm_bwd_ds_workspace_bytes per tile: 16 KB); a head needs one tile per (128-key tile,
+ * 64-row query tile) between the first and the last query tile that is not fully masked for that key tile,
+ * so the space grows with the unmasked pairs (about 2 bytes each for the document masks), not with N^2.
+ *
+ * fm_bwd_plan_bytes(B, H, Hm, N): device bytes of a plan (0 on bad sizes).
+ * fm_bwd_plan(bounds, B, H, Hm, N, causal, plan, stream): writes the plan of the mask into the caller's
+ *   device buffer `plan` (8-byte aligned, fm_bwd_plan_bytes long): per key tile its first live query
+ *   tile and its first slot, per head its region, and in the first 8 bytes the int64 number of tiles of
+ *   the whole problem. bounds as for fm_bwd (NULL when there are no vectors). A plan depends only on the
+ *   bounds, the sizes and the causal flag: recompute it when the mask changes. Asynchronous like every
+ *   call: read the total back (after synchronising) to size the workspace.
+ * fm_bwd_ds_workspace_bytes(dtype, B, H, N, d, tiles): fm_bwd_workspace_bytes plus `tiles` stored tiles
+ *   (0 on bad sizes or overflow).
+ * fm_bwd_ds(...): the arguments of fm_bwd plus the plan. The workspace holds D first (as fm_bwd) and
+ *   stored tiles in the rest: a head whose region fits gets its dS stored and its dq streamed; a head
+ *   that does not fit (or any head, for float32 inputs) runs as in fm_bwd. Every head meets the same
+ *   accuracy; results are bitwise reproducible for a given workspace size. The plan must come from
+ *   fm_bwd_plan with the same B, H, Hm and N (its size and layout follow from them); a plan of those sizes
+ *   whose content belongs to other bounds or another causal flag gives wrong results but never accesses
+ *   memory outside the plan, the workspace or the tensors.
+ * Errors: as fm_bwd; FM_ERR_INVALID for a NULL or misaligned plan. */
+size_t fm_bwd_plan_bytes(int B, int H, int Hm, int N);
+fm_status fm_bwd_plan(const int32_t* bounds, int B, int H, int Hm, int N, int causal, void* plan,
+                      hipStream_t stream);
+size_t fm_bwd_ds_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d, int64_t tiles);
+fm_status fm_bwd_ds(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                    const float* lse, fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts,
+                    const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds,
+                    const int32_t* sched, const void* plan, int causal, float scale, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* One block of query rows against all keys: the unit of work of one rank under context parallelism,
  * whose mask localisation is a zero-communication clip-shift-max on the boundary vectors that keeps the
  * single-GPU kernel (FlashMask-3 summary, readmex.ai, the quoted abstract in the "in-depth insights"

@@ -25,7 +25,8 @@ EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "
             "fm_tile_schedule", "fm_fwd",
             "fm_bwd_workspace_bytes", "fm_bwd", "fm_fwd_rows", "fm_bwd_rows", "fm_tile_classes",
             "fm_compact_keys", "fm_gather_rows", "fm_lsh_buckets", "fm_bucket_sort", "fm_fwd_mapped",
-            "fm_bwd_mapped", "fm_status_str")
+            "fm_bwd_mapped", "fm_bwd_plan_bytes", "fm_bwd_plan", "fm_bwd_ds_workspace_bytes", "fm_bwd_ds",
+            "fm_status_str")
 
 
 class FmError(RuntimeError):
@@ -64,6 +65,14 @@ def load_library(path: str = LIB_PATH):
     lib.fm_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fm_bwd.restype = I
     lib.fm_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P, S, P]
+    lib.fm_bwd_plan_bytes.restype = S
+    lib.fm_bwd_plan_bytes.argtypes = [I, I, I, I]
+    lib.fm_bwd_plan.restype = I
+    lib.fm_bwd_plan.argtypes = [P, I, I, I, I, I, P, P]
+    lib.fm_bwd_ds_workspace_bytes.restype = S
+    lib.fm_bwd_ds_workspace_bytes.argtypes = [I, I, I, I, I, ctypes.c_int64]
+    lib.fm_bwd_ds.restype = I
+    lib.fm_bwd_ds.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, P, I, F, P, P, P, P, S, P]
     lib.fm_tile_classes.restype = I
     lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
     lib.fm_fwd_mapped.restype = I
@@ -224,6 +233,56 @@ def fm_bwd(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, boun
     _check(lib.fm_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N, d,
                       *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), int(bool(causal)), float(scale), _ptr(dq),
                       _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)), "fm_bwd")
+    return dq, dk, dv
+
+
+def fm_bwd_plan_bytes(B: int, H: int, Hm: int, N: int) -> int:
+    return load_library().fm_bwd_plan_bytes(B, H, Hm, N)
+
+
+def fm_bwd_plan(bounds, B: int, H: int, Hm: int, N: int, causal: bool, plan=None, stream=None, device=None):
+    """Plan of the stored-dS backward (uint8 device tensor); plan_tiles() reads its tile count."""
+    lib = load_library()
+    _need_cuda(bounds, plan)
+    if plan is None:
+        dev = bounds.device if bounds is not None else (device or torch.device("cuda"))
+        plan = torch.empty(max(fm_bwd_plan_bytes(B, H, Hm, N), 8), dtype=torch.uint8, device=dev)
+    _check(lib.fm_bwd_plan(_ptr(bounds), B, H, Hm, N, int(bool(causal)), _ptr(plan), _stream(stream)),
+           "fm_bwd_plan")
+    return plan
+
+
+def plan_tiles(plan) -> int:
+    """Stored-dS tiles of the whole problem (the plan's first 8 bytes; synchronises with the device)."""
+    return int(plan[:8].view(torch.int64).item())
+
+
+def fm_bwd_ds_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int, tiles: int) -> int:
+    code = FM_BF16 if dtype == torch.bfloat16 else FM_F32
+    return load_library().fm_bwd_ds_workspace_bytes(code, B, H, N, d, int(tiles))
+
+
+def fm_bwd_ds(q, k, v, out, dout, lse, plan, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False,
+              scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, sched=None):
+    """(dq, dk, dv) as fm_bwd, with dq formed from stored dS tiles for the heads that fit in the workspace
+    (without a workspace, one sized from the plan's tile count is allocated)."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, out, dout, lse, bounds, sched, plan, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        need = fm_bwd_ds_workspace_bytes(q.dtype, B, H, N, d, plan_tiles(plan))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fm_bwd_ds(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N, d,
+                         *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), _ptr(plan), int(bool(causal)),
+                         float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                         _stream(stream)), "fm_bwd_ds")
     return dq, dk, dv
 
 

@@ -20,7 +20,13 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
                       const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
                       int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream, const int* qmap, const int* kmap);
+                      hipStream_t stream, const int* qmap, const int* kmap, void* ds_cache, long long ds_cap,
+                      const DsPlan* ds_plan);
+size_t ds_plan_bytes(int B, int H, int Hm, int N);
+DsPlan ds_plan_view(const void* plan, int B, int H, int Hm, int N);
+hipError_t launch_ds_plan(const int* bounds, int B, int H, int Hm, int N, int causal, void* plan,
+                          hipStream_t stream);
+int ds_tile_bytes();
 int fwd_qblock();
 hipError_t launch_tile_schedule(const int* bounds, int rows, int Nq, int Nk, int q_off, int causal, int* sched,
                                 hipStream_t stream);
@@ -160,7 +166,8 @@ fm_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
                    fm_dtype dtype, int B, int H, int Nq, int Nk, int q_off, int d, const int32_t* lts,
                    const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds,
                    const int32_t* sched, int causal, float scale, const int32_t* qmap, const int32_t* kmap,
-                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                   const void* plan = nullptr) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return FM_ERR_INVALID;
@@ -175,8 +182,18 @@ fm_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
   const size_t need = fm_bwd_workspace_bytes(dtype, B, H, Nq, d);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FM_ERR_WORKSPACE;
   float* dd = static_cast<float*>(workspace);
+  // Stored-dS mode: the workspace past D (a multiple of 256 bytes) holds whole dS tiles.
+  void* cache = nullptr;
+  long long cap = 0;
+  fm::DsPlan view{};
+  if (plan != nullptr) {
+    cache = static_cast<char*>(workspace) + need;
+    cap = (long long)((workspace_bytes - need) / (size_t)fm::ds_tile_bytes());
+    view = fm::ds_plan_view(plan, B, H, Hm, Nk);
+  }
   return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dd, lts, lte, uts, ute,
-                                 bounds, B, H, Nq, Nk, q_off, Hm, sched, causal != 0, scale, stream, qmap, kmap));
+                                 bounds, B, H, Nq, Nk, q_off, Hm, sched, causal != 0, scale, stream, qmap, kmap,
+                                 cache, cap, plan != nullptr ? &view : nullptr));
 }
 }  // namespace
 
@@ -206,6 +223,35 @@ fm_status fm_bwd(const void* q, const void* k, const void* v, const void* out, c
                  hipStream_t stream) {
   return fm_bwd_rows(q, k, v, out, dout, lse, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, sched,
                      causal, scale, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+size_t fm_bwd_plan_bytes(int B, int H, int Hm, int N) {
+  if (!sizes_ok(B, H, N) || (Hm != 1 && Hm != H)) return 0;
+  return fm::ds_plan_bytes(B, H, Hm, N);
+}
+
+fm_status fm_bwd_plan(const int32_t* bounds, int B, int H, int Hm, int N, int causal, void* plan,
+                      hipStream_t stream) {
+  if (plan == nullptr || (reinterpret_cast<uintptr_t>(plan) & 7u) != 0) return FM_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || (Hm != 1 && Hm != H)) return FM_ERR_INVALID;
+  return from_hip(fm::launch_ds_plan(bounds, B, H, Hm, N, causal != 0, plan, stream));
+}
+
+size_t fm_bwd_ds_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d, int64_t tiles) {
+  const size_t base = fm_bwd_workspace_bytes(dtype, B, H, N, d);
+  const size_t tb = (size_t)fm::ds_tile_bytes();
+  if (base == 0 || tiles < 0 || (uint64_t)tiles > (SIZE_MAX - base) / tb) return 0;
+  return base + (size_t)tiles * tb;
+}
+
+fm_status fm_bwd_ds(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                    fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts, const int32_t* lte,
+                    const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds, const int32_t* sched,
+                    const void* plan, int causal, float scale, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (plan == nullptr || (reinterpret_cast<uintptr_t>(plan) & 7u) != 0) return FM_ERR_INVALID;
+  return bwd_impl(q, k, v, out, dout, lse, dtype, B, H, N, N, 0, d, lts, lte, uts, ute, Hm, bounds, sched, causal,
+                  scale, nullptr, nullptr, dq, dk, dv, workspace, workspace_bytes, stream, plan);
 }
 
 fm_status fm_compact_keys(const int32_t* lts, const int32_t* lte, const int32_t* uts, const int32_t* ute, int B,

@@ -46,7 +46,18 @@ struct BwdArgs {
   // row j of dk and dv (written) is row kmap[j]. Rows outside the range are not written and read as zero.
   const int* qmap;
   const int* kmap;
+  // Stored-dS mode (ds_cache not null): heads whose region of the plan fits in ds_cap tiles get their dS
+  // tiles written by the dK/dV pass and their dq formed from them afterwards; for those heads the dq pass
+  // only forms D. Other heads run as without a cache.
+  char* ds_cache;
+  long long ds_cap;
+  DsPlan ds;
 };
+
+// Whether head (b, h) with mask row mrow has its dS tiles stored.
+__device__ __forceinline__ bool ds_stored(const BwdArgs& a, int bh, long long mrow) {
+  return a.ds_cache != nullptr && ds_head_stored(a.ds, a.ds_cap, bh, mrow);
+}
 
 // ------------------------------------------------------------------ 1. dQ (and D), query-tile parallel
 
@@ -113,6 +124,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
   const bool causal = a.causal != 0;
   const float sl2 = a.scale_log2;
 
+  // A head whose dS tiles are stored gets its dq from them later: here it only needs D.
+  const bool d_only = ds_stored(a, bh, (long long)b * a.Hm + hm);
   // Q^T and dO^T operands (k = d) for this lane's row, D_i and lse_i.
   typename M::frag qf[Tr::NQF], df[Tr::NQF];
   float part = 0.f;
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
   for (int c = 0; c < Tr::NQF; ++c) {
     if (row < Nq) {
       const size_t e = (size_t)row * D + c * M::KW + g * M::E;
-      qf[c] = load_kcontig_frag<T>(qg + e);
+      qf[c] = d_only ? typename M::frag{} : load_kcontig_frag<T>(qg + e);
       df[c] = load_kcontig_frag<T>(dog + e);
       const typename M::frag of = orow_ok ? load_kcontig_frag<T>(og + (size_t)orow * D + c * M::KW + g * M::E)
                                           : typename M::frag{};
@@ -144,6 +157,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
     lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
     if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;
   }
+  if (d_only) return;
 
   f32x16 acc[Tr::NDB];
 #pragma unroll
@@ -429,6 +443,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   rrd.init(lane);
   crd.init(lane);
 
+  // Stored-dS mode: role 1 writes each dS tile it forms (64 query rows x the workgroup's 128 keys) to slot
+  // ds_slot0 + (qt - ds_first) of the cache with four 16-byte stores per lane, each covering 1 KB
+  // contiguous: store (ib, p) of lane (g, l32) holds rows 32 ib + 16 p + 4 g + (0..3) and then
+  // 32 ib + 16 p + 8 + 4 g + (0..3) of its key, at position g * 32 + (l32 ^ (8 g + 4 p)).
+  static_assert(BC == DS_KEYS && BR == DS_QROWS, "stored dS tiles are the dK/dV pass's tiles");
+  const bool ds_on = role == 1 && ds_stored(a, bh, (long long)b * a.Hm + hm);
+  long long ds_slot0 = 0, ds_span = 0;  // tile qt goes to slot ds_slot0 + (qt - ds_first) when inside the span
+  int ds_first = 0;
+  int ds_off[2];
+  if (ds_on) {
+    const long long mrow = (long long)b * a.Hm + hm;
+    long long lo;
+    ds_span = ds_tile_span(a.ds, mrow, kt, lo);
+    ds_first = a.ds.first[mrow * a.ds.nkt + kt];
+    ds_slot0 = a.ds.region[bh] + lo;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) ds_off[p] = kgrp * 4096 + (g * 32 + (l32 ^ (8 * g + 4 * p))) * 16;
+
   // dV^T (role 0) or dK^T (role 1) for this lane's key column, all of d.
   f32x16 acc[Tr::NDB];
 #pragma unroll
@@ -468,8 +501,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     }
   };
 
-  // dK^T += Q^T dS for one query tile, dS in register order (role 1).
-  auto dk_products = [&](const bf16x4 (&sv)[2][4], const bf16* qb) {
+  // dK^T += Q^T dS for one query tile, dS in register order (role 1). With STORE, the tile's dS also goes
+  // to `st` (stored-dS mode), its 4 stores placed after products 1, 3, 5 and 7, so that they leave while
+  // the matrix cores work instead of holding up the end of the tile.
+  auto dk_products = [&](auto store_tag, const bf16x4 (&sv)[2][4], const bf16* qb, char* st) {
+    constexpr bool STORE = decltype(store_tag)::value;
+    constexpr int NM = 4 * Tr::NDB;  // products
+    static_assert(NM >= 8, "a store after every other product");
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bf16x8 sf;
@@ -479,10 +517,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         sf[4 + e] = sv[t >> 1][2 * (t & 1) + 1][e];
       }
 #pragma unroll
-      for (int db = 0; db < Tr::NDB; ++db) acc[db] = M::mma(crd.read(qb, t, db), sf, acc[db]);
+      for (int db = 0; db < Tr::NDB; ++db) {
+        acc[db] = M::mma(crd.read(qb, t, db), sf, acc[db]);
+        if constexpr (STORE) {
+          const int m = t * Tr::NDB + db;
+          if ((m & 1) && m < 8) {
+            const int ib = m >> 2, p = (m >> 1) & 1;  // store k = (m - 1) / 2 = 2 ib + p
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[e] = sv[ib][2 * p][e];
+              w[4 + e] = sv[ib][2 * p + 1][e];
+            }
+            // non-temporal: the tile is read back once, by the dq pass, and should not evict Q / dO tiles
+            i32x4 wi;
+            __builtin_memcpy(&wi, &w, 16);
+            __builtin_nontemporal_store(wi, reinterpret_cast<i32x4*>(st + (2 * ib + p) * 1024 + ds_off[p]));
+          }
+        }
+      }
     }
-    interleave_reads<4 * Tr::NDB, 8 * Tr::NDB, 4>();
+    if constexpr (STORE) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, (8 * Tr::NDB - 4 + NM - 1) / NM, 0);
+        if ((m & 1) && m < 8) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
+      }
+    } else {
+      interleave_reads<4 * Tr::NDB, 8 * Tr::NDB, 4>();
+    }
   };
+
 
   TileWindow win = empty_window();
   int qt = next_live_tile(win, qt_begin, nq, class_of, lane);
@@ -490,7 +557,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   int qs = 0, ds = 0;     // ring slots of the current tile's Q and dO (and lse / D)
   int qs_prev = -1;       // role 1: slot of the previous tile's Q, whose dS is still pending
   bf16x4 sv[2][4];        // role 1: that dS, register order
+  char* st_prev = nullptr;  // role 1: that dS's destination in the cache (stored-dS mode), or null
+  // dK products of the previous tile, storing its dS on the way when it has a destination
+  auto dk_pass = [&](const bf16* qb) {
+    if (st_prev != nullptr) {
+      dk_products(Flag<true>{}, sv, qb, st_prev);
+    } else {
+      dk_products(Flag<false>{}, sv, qb, nullptr);
+    }
+  };
 
+  // Every load issued so far (K or V fragments, mask values, bounds, plan entries, the first tile) is
+  // first used inside the loop. Left pending at the loop's entry, the compiler's wait-count analysis
+  // carries them into every iteration as in-loop vmcnt waits, which also catch the untracked tile copies
+  // issued between the products and stall each tile on their latency.
+  __builtin_amdgcn_s_waitcnt(0);
   while (qt < nq) {
     const int q0 = qt * BR;
     const bool need_mask = window_partial(win, qt) || (q0 + BR > Nq) || (c0 + BC > N);
@@ -570,7 +651,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     } else {
       // above the default priority of the other roles' arithmetic, below role 0's products
       __builtin_amdgcn_s_setprio(1);
-      if (qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
+      if (qs_prev >= 0) dk_pass(q_lds + qs_prev * TILE);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         x[ib] = zero16();
@@ -612,6 +693,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
           for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)p4[e] * (x[ib][4 * q4 + e] - dd4[e]));
         }
       }
+      st_prev = (ds_on && qt >= ds_first && (long long)(qt - ds_first) < ds_span)
+                    ? a.ds_cache + (ds_slot0 + (qt - ds_first)) * DS_TILE_BYTES
+                    : nullptr;
       qs_prev = qs;
     }
     qt = qt_next;
@@ -620,7 +704,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // Role 1: the dK products of the last tile (its Q is still in LDS: nothing has been stored since).
-  if (role == 1 && qs_prev >= 0) dk_products(sv, q_lds + qs_prev * TILE);
+  if (role == 1 && qs_prev >= 0) dk_pass(q_lds + qs_prev * TILE);
 
   // dV = dV^T (role 0) or dK = scale * dK^T (role 1) for this lane's key column, all of d.
   const int jo = (a.kmap != nullptr && j < N) ? a.kmap[(size_t)bh * N + j] : j;  // the row written
@@ -783,6 +867,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ host launch
 
+hipError_t launch_dq_stream(int d, const void* k, const void* ds, long long cap, const DsPlan& plan, void* dq,
+                            const int* bounds, int B, int H, int Hm, int N, int causal, float scale,
+                            hipStream_t stream);
+
 template <typename T, int D>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
   const long nq = (a.Nq + DqTraits<T, D>::BR - 1) / DqTraits<T, D>::BR;
@@ -792,6 +880,12 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
   const long nkt = (a.Nk + 127) / 128;
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)(nkt * a.B * a.H)), dim3(512), 0, stream, a);
+    if (a.ds_cache != nullptr) {
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_dq_stream(D, a.k, a.ds_cache, a.ds_cap, a.ds, a.dq, a.bounds, a.B, a.H, a.Hm, a.Nk, a.causal,
+                              a.scale, stream);
+    }
   } else {
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((unsigned)(nkt * a.B * a.H)), dim3(256), 0, stream, a);
   }
@@ -802,7 +896,8 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
                       const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
                       int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream, const int* qmap, const int* kmap) {
+                      hipStream_t stream, const int* qmap, const int* kmap, void* ds_cache, long long ds_cap,
+                      const DsPlan* ds_plan) {
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.dd = dd;
   a.dq = dq; a.dk = dk; a.dv = dv;
@@ -818,6 +913,9 @@ hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const v
   a.scale_log2 = scale * LOG2E;
   a.qmap = qmap;
   a.kmap = kmap;
+  a.ds_cache = bf16_in ? static_cast<char*>(ds_cache) : nullptr;  // float32 keeps the recomputing dq pass
+  a.ds_cap = ds_cap;
+  a.ds = ds_plan != nullptr ? *ds_plan : DsPlan{};
   if (bf16_in) return d == 64 ? launch_bwd_t<bf16, 64>(a, stream) : launch_bwd_t<bf16, 128>(a, stream);
   return d == 64 ? launch_bwd_t<float, 64>(a, stream) : launch_bwd_t<float, 128>(a, stream);
 }

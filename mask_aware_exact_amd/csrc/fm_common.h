@@ -28,6 +28,12 @@ constexpr int KBLOCK = 64;  // key columns per bounds entry
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// A compile-time flag passed as an argument (selects a variant of a generic lambda).
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
+};
+
 enum TileClass : int { CLS_NONE = 0, CLS_PARTIAL = 1, CLS_FULL = 2 };
 
 // Per-key-tile bounds (min/max of each of LTS, LTE, UTS, UTE over the tile's columns). Named fields
@@ -73,6 +79,40 @@ __device__ inline TileBounds merged_bounds(const int* __restrict__ brow, int kt0
     r.ute_max = max(r.ute_max, q[7]);
   }
   return r;
+}
+
+// Device view of a stored-dS plan (written by the plan pass of the stored-dS backward): per (b, hm, 128-key
+// tile) the first live 64-row query tile and the tile's first slot inside its head's region, per (b, hm)
+// the slots of one head, and per (b, h) the region's first slot. Slots are counted in 16 KB tiles.
+constexpr int DS_QROWS = 64;                         // query rows of a stored dS tile
+constexpr int DS_KEYS = 128;                         // keys of a stored dS tile
+constexpr int DS_TILE_BYTES = DS_QROWS * DS_KEYS * 2;  // bf16
+
+struct DsPlan {
+  long long* total;     // [1]: slots of the whole problem
+  long long* region;    // [B * H]
+  long long* base;      // [B * Hm * nkt]
+  long long* rowtotal;  // [B * Hm]
+  int* first;           // [B * Hm * nkt]
+  int nkt;              // 128-key tiles per row
+};
+
+// Whether head (bh) with mask row mrow has its dS tiles stored: its region fits in the first `cap` slots.
+__device__ __forceinline__ bool ds_head_stored(const DsPlan& p, long long cap, int bh, long long mrow) {
+  const long long r = p.region[bh], t = p.rowtotal[mrow];
+  return r >= 0 && t >= 0 && r <= cap - t;
+}
+
+// Slots of key tile kt inside its head's region: [lo, lo + span) with span returned. A plan whose entries
+// are inconsistent gives span 0, so that a plan that does not belong to the problem can give wrong
+// results but never an access outside the head's region.
+__device__ __forceinline__ long long ds_tile_span(const DsPlan& p, long long mrow, int kt, long long& lo) {
+  const long long e = mrow * p.nkt + kt;
+  const long long t = p.rowtotal[mrow];
+  const long long b0 = p.base[e];
+  const long long b1 = kt + 1 < p.nkt ? p.base[e + 1] : t;
+  lo = b0;
+  return (b0 >= 0 && b1 >= b0 && b1 <= t) ? b1 - b0 : 0;
 }
 
 // Rows of a query work unit (forward, dq) and columns of a key work unit (dk, dv): the granule of the
@@ -413,6 +453,11 @@ struct SwzColReads {  // operand with k along the rows (the load_kmajor_frag pat
 // the tile; the compiler only ever over-waits for its own loads because of these untracked ones.
 __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
+}
+
+// lds_copy16 for data read once (streaming): the non-temporal hint keeps it from displacing reused lines.
+__device__ __forceinline__ void lds_copy16_nt(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
 
 // Direct global-to-LDS load of 4 bytes per lane (256 bytes per wave instruction, lane-linear at `lds`).
