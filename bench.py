@@ -1,17 +1,21 @@
 """Benchmark: column-wise-mask (FlashMask) attention forward + backward on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input:
-fm_tile_bounds -> fm_fwd -> fm_bwd (with --schedule, fm_tile_schedule before fm_fwd and both kernels
-launched in its order). The metric counts only unmasked FLOPs:
+fm_tile_bounds -> fm_bwd_plan -> fm_fwd -> fm_bwd_ds (the backward that forms dQ from stored dS tiles; the
+workspace for them is sized once from the plan before timing). With --bwd recompute the step is
+fm_tile_bounds -> fm_fwd -> fm_bwd instead; with --schedule, fm_tile_schedule runs after the bounds and
+the kernels launch in its order. The metric counts only unmasked FLOPs:
     FLOP per step = 14 * d * U   (forward 4 d U: Q K^T and P V; backward 10 d U: the S recompute,
                                   dP, dV, dK and dQ products), U = unmasked (query, key) pairs.
 The default workload is the long-context configuration with a causal document mask (B=1, H=8,
 N=131072, d=128, bf16; document lengths log-uniform in [1K, 32K]), the largest head-dim-128 workload.
 
 Prints one JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --no-cpu-baseline,
---schedule (launch in the longest-first order of fm_tile_schedule, computed inside each step),
---sweep (also time the other head-dim-128 workloads, a few steps each, with and without the schedule,
-reported under "sweep"),
+--schedule, --bwd {stored, recompute},
+--sweep (also time every (config, mask) workload a few steps each with both backward forms, the
+context-parallel rank shares, key compaction and the hash workloads, reported under "sweep"; with
+--records FILE one JSON line per (config, mask) workload is written there, and --parity FILE merges the
+whole-tensor parity errors and oracle timings that the full-size GPU tests write),
 --copy-calibration (after timing, one 1 GiB device-to-device copy, the reference kernel for scaling
 hardware byte counters in profiling runs).
 """
@@ -50,9 +54,9 @@ WORKLOADS = {
 }
 DEFAULT_WORKLOAD = "long_context_causal_document"
 ROOFLINE_KERNEL = "fm_bwd"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fm_bwd_long_context_causal_document_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fm_bwd_ds_long_context_causal_document_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "mask_aware_exact_amd", "csrc", f)
-                  for f in ("fm_common.h", "fm_bwd.hip")]
+                  for f in ("fm_common.h", "fm_bwd.hip", "fm_dstore.hip")]
 
 
 def kernel_source_digest() -> str:
@@ -64,9 +68,9 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per fm_bwd call from the committed counter summary, or None when that summary is
-    missing, covers another workload, or was taken from other kernel sources."""
+def measured_traffic(workload: str, call: str = "fm_bwd_ds"):
+    """HBM bytes per backward call from the committed counter summary, or None when that summary is
+    missing, covers another workload or call, or was taken from other kernel sources."""
     try:
         fields = {}
         with open(TRAFFIC_FILE) as f:
@@ -75,6 +79,8 @@ def measured_traffic(workload: str):
                     k, v = line[2:].split(":", 1)
                     fields[k.strip()] = v.strip().strip("`")
         if fields.get("workload") != workload or fields.get("kernel_source_digest") != kernel_source_digest():
+            return None
+        if fields.get("call", "fm_bwd") != call:
             return None
         return int(float(fields["hbm_bytes_per_call"]))
     except (OSError, KeyError, ValueError):
@@ -184,56 +190,74 @@ def balanced_row_blocks(spec: W.MaskSpec, H: int, ranks: int, align: int = 128):
     return cuts
 
 
-def time_workload(fm, wl: Workload, steps: int, warmup: int, use_sched: bool = False):
+def time_workload(fm, wl: Workload, steps: int, warmup: int, use_sched: bool = False, stored: bool = True):
     """One step = fm_tile_bounds (when the mask has vectors), fm_tile_schedule (longest-first dispatch
-    order, only with use_sched), fm_fwd, fm_bwd; all of it timed. Returns the wall time of the
-    timed steps, the mean per-part milliseconds (bounds, schedule, fwd, bwd) and a finiteness flag."""
+    order, only with use_sched), then with `stored` fm_bwd_plan, fm_fwd and fm_bwd_ds (dQ from stored dS
+    tiles, workspace sized once from the plan before timing), else fm_fwd and fm_bwd (dQ recomputed); all
+    of it timed. Returns the wall time of the timed steps, the mean per-part milliseconds (bounds,
+    schedule, plan, fwd, bwd) and a finiteness flag."""
     import torch
     dev = wl.q.device
     stream = torch.cuda.current_stream(dev)
-    bounds = torch.empty(fm.fm_bounds_elems(wl.B, wl.spec.Hm, wl.N) or 8, dtype=torch.int32, device=dev)
-    sched_buf = torch.empty(fm.fm_schedule_elems(wl.B, wl.spec.Hm, wl.N, wl.N), dtype=torch.int32, device=dev)
+    B, H, Hm, N, d = wl.B, wl.H, wl.spec.Hm, wl.N, wl.d
+    bounds = torch.empty(fm.fm_bounds_elems(B, Hm, N) or 8, dtype=torch.int32, device=dev)
+    sched_buf = torch.empty(fm.fm_schedule_elems(B, Hm, N, N), dtype=torch.int32, device=dev)
     out = torch.empty_like(wl.q)
-    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
-    ws = torch.empty(fm.fm_bwd_workspace_bytes(torch.bfloat16, wl.B, wl.H, wl.N, wl.d), dtype=torch.uint8,
-                     device=dev)
+    plan = None
+    if stored:
+        b0 = fm.fm_tile_bounds(*wl.vecs, B, Hm, N, bounds=bounds) if wl.has_vecs else None
+        plan = fm.fm_bwd_plan(b0, B, H, Hm, N, wl.spec.causal, device=dev)
+        ws_bytes = fm.fm_bwd_ds_workspace_bytes(torch.bfloat16, B, H, N, d, fm.plan_tiles(plan))
+    else:
+        ws_bytes = fm.fm_bwd_workspace_bytes(torch.bfloat16, B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
         b = None
         if wl.has_vecs:
-            b = fm.fm_tile_bounds(*wl.vecs, wl.B, wl.spec.Hm, wl.N, bounds=bounds)
+            b = fm.fm_tile_bounds(*wl.vecs, B, Hm, N, bounds=bounds)
         if evs is not None:
             evs[1].record(stream)
         sc = None
         if use_sched:
-            sc = fm.fm_tile_schedule(b, wl.B, wl.spec.Hm, wl.N, wl.N, wl.spec.causal, sched=sched_buf)
+            sc = fm.fm_tile_schedule(b, B, Hm, N, N, wl.spec.causal, sched=sched_buf)
         if evs is not None:
             evs[2].record(stream)
+        if stored:
+            fm.fm_bwd_plan(b, B, H, Hm, N, wl.spec.causal, plan=plan)
+        if evs is not None:
+            evs[3].record(stream)
         fm.fm_fwd(wl.q, wl.k, wl.v, *wl.vecs, bounds=b, sched=sc, causal=wl.spec.causal, scale=wl.scale, out=out,
                   lse=lse)
         if evs is not None:
-            evs[3].record(stream)
-        fm.fm_bwd(wl.q, wl.k, wl.v, out, wl.do, lse, *wl.vecs, bounds=b, sched=sc, causal=wl.spec.causal,
-                  scale=wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
-        if evs is not None:
             evs[4].record(stream)
+        if stored:
+            fm.fm_bwd_ds(wl.q, wl.k, wl.v, out, wl.do, lse, plan, *wl.vecs, bounds=b, sched=sc,
+                         causal=wl.spec.causal, scale=wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            fm.fm_bwd(wl.q, wl.k, wl.v, out, wl.do, lse, *wl.vecs, bounds=b, sched=sc, causal=wl.spec.causal,
+                      scale=wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if evs is not None:
+            evs[5].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    parts = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])  # ms
+    parts = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(5)] for e in events])  # ms
     ok = bool(torch.isfinite(out.float()).all() and torch.isfinite(dq.float()).all()
               and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all())
+    del ws
     return wall, parts.mean(axis=0), ok
 
 
@@ -475,6 +499,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--schedule", action="store_true",
                     help="compute the longest-first dispatch schedule each step and launch in its order")
+    ap.add_argument("--bwd", choices=("stored", "recompute"), default="stored",
+                    help="backward: fm_bwd_ds (dQ from stored dS tiles, the default) or fm_bwd (dQ recomputed)")
+    ap.add_argument("--records", default=None,
+                    help="with --sweep: write one JSON line per (config, mask) workload to this file")
+    ap.add_argument("--parity", default=None,
+                    help="with --records: merge the whole-tensor parity results (JSON by workload) into the records")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -509,11 +539,15 @@ def main():
 
     wl = Workload(args.workload, dev)
     use_sched = args.schedule
-    wall, parts_ms, ok = time_workload(fm, wl, args.steps, args.warmup, use_sched)
+    stored = args.bwd == "stored"
+    wall, parts_ms, ok = time_workload(fm, wl, args.steps, args.warmup, use_sched, stored)
     ms_per_step = wall * 1e3 / args.steps
     tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
-    bwd_ms = float(parts_ms[3])
+    bwd_ms = float(parts_ms[4])
     bwd_tflops = wl.flop_bwd / (bwd_ms * 1e-3) / 1e12
+    bwd_name = "fm_bwd_ds" if stored else "fm_bwd"
+    bwd_kernels = ("fm_bwd_ds (bwd_dq_kernel forming D only, bwd_dkdv_pair_kernel storing dS, dq_stream_kernel)"
+                   if stored else "fm_bwd (bwd_dq_kernel then bwd_dkdv_pair_kernel)")
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -531,18 +565,22 @@ def main():
                    "causal": bool(wl.spec.causal), "unmasked_pairs": int(wl.U),
                    "flop_per_step": wl.flop, "flop_formula": "14*d*U"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "peak_tflops_used": PEAK_BF16_TFLOPS,
         "schedule": "longest-first" if use_sched else "default order",
+        "backward": "stored dS (fm_bwd_plan + fm_bwd_ds)" if stored else "recomputed dQ (fm_bwd)",
         "parts_ms": {"fm_tile_bounds": round(float(parts_ms[0]), 4),
                      "fm_tile_schedule": round(float(parts_ms[1]), 4) if use_sched else None,
-                     "fm_fwd": round(float(parts_ms[2]), 4),
-                     "fm_bwd": round(bwd_ms, 4)},
-        "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[2] * 1e-3) / 1e12, 2),
-                         "fm_bwd": round(bwd_tflops, 2)},
+                     "fm_bwd_plan": round(float(parts_ms[2]), 4) if stored else None,
+                     "fm_fwd": round(float(parts_ms[3]), 4),
+                     bwd_name: round(bwd_ms, 4)},
+        "parts_tflops": {"fm_fwd": round(wl.flop_fwd / (parts_ms[3] * 1e-3) / 1e12, 2),
+                         bwd_name: round(bwd_tflops, 2)},
         "finite_outputs": ok,
         "prepass": prepass_record(fm, wl, float(parts_ms[0]), dev),
-        "roofline": {"bound": "mfma", "kernel": "fm_bwd (bwd_dq_kernel then bwd_dkdv_pair_kernel)",
+        "roofline": {"bound": "mfma", "kernel": bwd_kernels,
                      "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(wl.name),
+                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name, bwd_name),
                      "flop_per_call": wl.flop_bwd, "flop_formula": "10*d*U"},
     }
     if args.copy_calibration:
@@ -557,26 +595,44 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads, args.cpu_tokens)
     if args.sweep:
         sweep = {}
+        parity = {}
+        if args.parity:
+            with open(args.parity) as f:
+                parity = json.load(f)
+        records = []
         for name in WORKLOADS:
-            if name == wl.name:
-                continue
             print(f"sweep: {name}", file=sys.stderr, flush=True)
-            del wl
-            torch.cuda.empty_cache()
-            wl = Workload(name, dev)
+            if name != wl.name:
+                del wl
+                torch.cuda.empty_cache()
+                wl = Workload(name, dev)
             n = max(3, args.steps // 4)
-            w2, p2, ok2 = time_workload(fm, wl, n, 1, use_sched)
-            w0, p0, _ = time_workload(fm, wl, n, 1, not use_sched)
+            w2, p2, ok2 = time_workload(fm, wl, n, 1, use_sched, True)
+            w0, p0, _ = time_workload(fm, wl, n, 1, use_sched, False)
             ms = w2 * 1e3 / n
-            sweep[name] = {"TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
-                           "d": wl.d, "U": int(wl.U), "fwd_ms": round(float(p2[2]), 3), "bwd_ms": round(float(p2[3]), 3),
-                           "bounds_ms": round(float(p2[0]), 4),
-                           "schedule_ms": round(float(p2[1] if use_sched else p0[1]), 4),
-                           "finite": ok2,
-                           ("ms_per_step_default_order" if use_sched else "ms_per_step_longest_first"):
-                               round(w0 * 1e3 / n, 3),
-                           ("fwd_bwd_ms_default_order" if use_sched else "fwd_bwd_ms_longest_first"):
-                               [round(float(p0[2]), 3), round(float(p0[3]), 3)]}
+            nvec = sum(v is not None for v in wl.vecs)
+            bb = bounds_bytes(wl.B, wl.spec.Hm, wl.N, nvec) if nvec else 0
+            r = {"workload": name, "config_index": wl.cfg.index, "mask": wl.mask, "B": wl.B, "H": wl.H,
+                 "N": wl.N, "d": wl.d, "dtype": "bf16", "U": int(wl.U), "flop_per_step": wl.flop,
+                 "t_bounds_us": round(float(p2[0]) * 1e3, 2), "t_plan_us": round(float(p2[2]) * 1e3, 2),
+                 "t_fwd_ms": round(float(p2[3]), 4), "t_bwd_ms": round(float(p2[4]), 4),
+                 "ms_per_step": round(ms, 4), "TFLOP/s": round(wl.flop / (ms * 1e-3) / 1e12, 2),
+                 "pct_of_peak": round(100.0 * wl.flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                 "fwd_TFLOP/s": round(wl.flop_fwd / (float(p2[3]) * 1e-3) / 1e12, 2),
+                 "bwd_TFLOP/s": round(wl.flop_bwd / (float(p2[4]) * 1e-3) / 1e12, 2),
+                 "prepass_GB/s": round(bb / (float(p2[0]) * 1e-3) / 1e9, 1) if nvec else None,
+                 "t_bwd_recompute_ms": round(float(p0[4]), 4),
+                 "ms_per_step_recompute": round(w0 * 1e3 / n, 4),
+                 "finite": ok2, "schedule": "longest-first" if use_sched else "default order",
+                 "steps": n}
+            r.update(parity.get(name, {}))
+            records.append(r)
+            sweep[name] = {k: r[k] for k in ("TFLOP/s", "pct_of_peak", "ms_per_step", "t_fwd_ms", "t_bwd_ms",
+                                              "t_bwd_recompute_ms")}
+        if args.records:
+            with open(args.records, "w") as f:
+                for r in records:
+                    f.write(json.dumps(r) + "\n")
         # one context-parallel rank's share at its real shape: the long-context workload over 8 ranks,
         # each rank's contiguous 16384 query rows against all keys
         del wl

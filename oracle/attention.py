@@ -60,6 +60,38 @@ def _row_block(N):
     return 256 if N <= 8192 else (128 if N <= 32768 else 64)
 
 
+def fwd_bwd_head_rows(q, k, v, do, vecs, causal, scale, r0, r1, row_block=None):
+    """Query rows [r0, r1) of one head (q, k, v, do [N, d] float64): out, lse, dq of those rows and their
+    contributions to dk, dv over [c_lo, c_hi), the column span holding every key they attend.
+    Returns (out, lse, dq, c_lo, dk_part, dv_part). Summed over a partition of the rows, the parts give
+    the whole dk and dv."""
+    N, d = q.shape
+    rb = row_block or _row_block(N)
+    out = np.zeros((r1 - r0, d))
+    lse = np.full(r1 - r0, -np.inf)
+    dq = np.zeros((r1 - r0, d))
+    dk = np.zeros((N, d))
+    dv = np.zeros((N, d))
+    lo, hi = N, 0
+    for a in range(r0, r1, rb):
+        b = min(r1, a + rb)
+        masked = dense_masked_rows(*vecs, causal, N, a, b)
+        live_cols = np.flatnonzero(~masked.all(axis=0))
+        if live_cols.size == 0:
+            continue
+        c0, c1 = int(live_cols[0]), int(live_cols[-1]) + 1
+        res = attend_rows(q[a:b], k[c0:c1], v[c0:c1], do[a:b], masked[:, c0:c1], scale)
+        out[a - r0:b - r0] = res["out"]
+        lse[a - r0:b - r0] = res["lse"]
+        dq[a - r0:b - r0] = res["dq"]
+        dk[c0:c1] += scale * (res["dS"].T @ q[a:b])
+        dv[c0:c1] += res["P"].T @ do[a:b]
+        lo, hi = min(lo, c0), max(hi, c1)
+    if hi <= lo:
+        return out, lse, dq, 0, dk[:0], dv[:0]
+    return out, lse, dq, lo, dk[lo:hi], dv[lo:hi]
+
+
 def fwd_bwd_head(q, k, v, do, vecs, causal, scale, row_block=None):
     """Full forward and backward of one head. q, k, v, do [N, d]; vecs = (lts, lte, uts, ute) 1-D or None.
 
@@ -69,25 +101,39 @@ def fwd_bwd_head(q, k, v, do, vecs, causal, scale, row_block=None):
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     N, d = q.shape
-    rb = row_block or _row_block(N)
+    out, lse, dq, lo, dkp, dvp = fwd_bwd_head_rows(q, k, v, do, vecs, causal, scale, 0, N, row_block)
+    dk = np.zeros((N, d))
+    dv = np.zeros((N, d))
+    dk[lo:lo + dkp.shape[0]] = dkp
+    dv[lo:lo + dvp.shape[0]] = dvp
+    return out, lse, dq, dk, dv
+
+
+def fwd_bwd_head_parallel(q, k, v, do, vecs, causal, scale, pool, chunk_rows):
+    """fwd_bwd_head with the rows split into chunks of chunk_rows run on a thread pool (NumPy releases the
+    GIL inside its kernels; the caller limits BLAS to one thread per call). Same result up to the order
+    of the float64 sums over row chunks."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    N, d = q.shape
     out = np.zeros((N, d))
     lse = np.full(N, -np.inf)
     dq = np.zeros((N, d))
     dk = np.zeros((N, d))
     dv = np.zeros((N, d))
-    for r0 in range(0, N, rb):
-        r1 = min(N, r0 + rb)
-        masked = dense_masked_rows(*vecs, causal, N, r0, r1)
-        live_cols = np.flatnonzero(~masked.all(axis=0))
-        if live_cols.size == 0:
-            continue
-        c0, c1 = int(live_cols[0]), int(live_cols[-1]) + 1
-        res = attend_rows(q[r0:r1], k[c0:c1], v[c0:c1], do[r0:r1], masked[:, c0:c1], scale)
-        out[r0:r1] = res["out"]
-        lse[r0:r1] = res["lse"]
-        dq[r0:r1] = res["dq"]
-        dk[c0:c1] += scale * (res["dS"].T @ q[r0:r1])
-        dv[c0:c1] += res["P"].T @ do[r0:r1]
+    starts = list(range(0, N, chunk_rows))
+    futs = {pool.submit(fwd_bwd_head_rows, q, k, v, do, vecs, causal, scale, a, min(N, a + chunk_rows)): a
+            for a in starts}
+    from concurrent.futures import as_completed
+    for f in as_completed(futs):
+        a = futs[f]
+        o, l_, gq, lo, dkp, dvp = f.result()
+        b = a + o.shape[0]
+        out[a:b], lse[a:b], dq[a:b] = o, l_, gq
+        dk[lo:lo + dkp.shape[0]] += dkp
+        dv[lo:lo + dvp.shape[0]] += dvp
     return out, lse, dq, dk, dv
 
 

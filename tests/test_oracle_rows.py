@@ -47,3 +47,19 @@ def test_row_blocks_reassemble_the_whole_problem(family, cuts):
         dv_sum += gv
     assert np.max(np.abs(dk_sum - dk)) <= 1e-12
     assert np.max(np.abs(dv_sum - dv)) <= 1e-12
+
+
+def test_chunked_head_equals_whole_head():
+    """The row-chunked driver of the full-size checks sums the same float64 terms as fwd_bwd_head."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import attention as OA
+    import workloads as W
+    rng = np.random.default_rng(11)
+    N, d = 700, 64
+    spec = W.make_mask(2, "causal_document", 1, 1, N, 0)
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    ref = OA.fwd_bwd_head(q, k, v, do, spec.column_slice(0, 0), spec.causal, 0.125)
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        got = OA.fwd_bwd_head_parallel(q, k, v, do, spec.column_slice(0, 0), spec.causal, 0.125, pool, 96)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12, equal_nan=True)
