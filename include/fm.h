@@ -12,9 +12,9 @@
  * row with every key masked yields out = 0, lse = -inf, a zero dq row and no dk/dv contribution.
  *
  * Tiles whose every (row, column) is masked are skipped and tiles with no masked entry run without
- * the elementwise mask ("kernel optimizations that eliminate unnecessary computations by leveraging
- * sparsity ... without sacrificing computational accuracy", FlashMask abstract). The result does not
- * depend on the classification: it only decides which work is done.
+ * the elementwise mask: the kernels use the mask's sparsity to drop work, at no cost in accuracy
+ * (FlashMask abstract). The result does not depend on the classification: it only decides which work
+ * is done.
  *
  * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library keeps no pointer after
@@ -53,10 +53,20 @@ typedef enum {
                              scale not finite and positive, vectors without bounds, qblock not positive */
   FM_ERR_UNSUPPORTED = 2, /* d not in {64, 128} or unknown dtype */
   FM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fm_bwd_workspace_bytes() */
-  FM_ERR_LAUNCH = 4       /* the HIP runtime reported an error for a launch */
+  FM_ERR_LAUNCH = 4,      /* the HIP runtime reported an error for a launch */
+  /* range markers, never returned: every int is a value of the type, so a value the library does not
+   * know (fm_status_str of an arbitrary int) is handled rather than undefined */
+  FM_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  FM_STATUS_RANGE_MAX_ = 2147483647
 } fm_status;
 
-typedef enum { FM_BF16 = 0, FM_F32 = 1 } fm_dtype;
+typedef enum {
+  FM_BF16 = 0,
+  FM_F32 = 1,
+  /* range markers, not dtypes: an unknown dtype value is FM_ERR_UNSUPPORTED rather than undefined */
+  FM_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  FM_DTYPE_RANGE_MAX_ = 2147483647
+} fm_dtype;
 
 /* Largest N accepted by every call (row and column indices stay within int32 arithmetic). */
 #define FM_MAX_N (1 << 24)
@@ -260,8 +270,9 @@ fm_status fm_bucket_sort(const int32_t* qbucket, const int32_t* kbucket, int B, 
  *   fm_fwd_mapped writes out[b][h][omap[r]] = row r of the result; lse stays at row r.
  *   fm_bwd_mapped reads out through qmap (out as fm_fwd_mapped wrote it), writes dq[b][h][qmap[r]] and
  *   dk, dv [b][h][kmap[c]]. Values equal fm_fwd / fm_bwd followed by the gathers with qpos / kpos, bit for
- *   bit. A map entry outside [0, N) drops that row: nothing is written for it, and the backward reads
- *   its out row as zero, so that query still adds to dk and dv with a zero row term D. With a map that is
+ *   bit. A map entry outside [0, N) drops that row: nothing is written for it, and in the backward a
+ *   query row whose qmap entry is out of range contributes nothing to dk and dv (as if its dout were
+ *   zero). With a map that is
  *   not a permutation, rows not hit keep their previous contents, and two entries naming the same row
  *   race (which of the two values remains is unspecified). out, dq, dk, dv must not overlap the inputs.
  * bf16 and float32, as fm_fwd / fm_bwd. Errors: as fm_fwd / fm_bwd; FM_ERR_INVALID for a NULL map. */

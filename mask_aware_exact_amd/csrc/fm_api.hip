@@ -6,42 +6,8 @@
 
 #include "fm.h"
 #include "fm_common.h"
+#include "fm_launch.h"
 
-namespace fm {
-hipError_t launch_tile_bounds(const int* lts, const int* lte, const int* uts, const int* ute, int rows, int N,
-                              int* bounds, hipStream_t stream);
-hipError_t launch_tile_classes(const int* bounds, int rows, int N, int causal, int qblock, uint8_t* classes,
-                               hipStream_t stream);
-hipError_t launch_fwd(bool bf16_in, int d, const void* q, const void* k, const void* v, void* out, float* lse,
-                      const int* lts, const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H,
-                      int Nq, int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream, const int* omap);
-hipError_t launch_bwd(bool bf16_in, int d, const void* q, const void* k, const void* v, const void* out,
-                      const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dd, const int* lts,
-                      const int* lte, const int* uts, const int* ute, const int* bounds, int B, int H, int Nq,
-                      int Nk, int q_off, int Hm, const int* sched, int causal, float scale,
-                      hipStream_t stream, const int* qmap, const int* kmap, void* ds_cache, long long ds_cap,
-                      const DsPlan* ds_plan);
-size_t ds_plan_bytes(int B, int H, int Hm, int N);
-DsPlan ds_plan_view(const void* plan, int B, int H, int Hm, int N);
-hipError_t launch_ds_plan(const int* bounds, int B, int H, int Hm, int N, int causal, void* plan,
-                          hipStream_t stream);
-int ds_tile_bytes();
-int fwd_qblock();
-hipError_t launch_tile_schedule(const int* bounds, int rows, int Nq, int Nk, int q_off, int causal, int* sched,
-                                hipStream_t stream);
-hipError_t launch_compact_keys(const int* lts, const int* lte, const int* uts, const int* ute, int rows, int N,
-                               int causal, int* kidx, int* kpos, int* counts, int* lts2, int* lte2, int* uts2,
-                               int* ute2, hipStream_t stream);
-hipError_t launch_gather_rows(const void* x, const int* idx, int B, int H, int Hm, int N, int row_bytes, void* y,
-                              hipStream_t stream);
-int lsh_max_nb();
-int sort_max_nb();
-hipError_t launch_lsh_buckets(bool bf16_in, int d, const void* x, const float* rot, int B, int H, int N, int Hr,
-                              int nb, int* out, hipStream_t stream);
-hipError_t launch_bucket_sort(const int* qb, const int* kb, int rows, int N, int nb, int* qidx, int* qpos,
-                              int* kidx, int* kpos, int* lts, int* lte, int* uts, int* ute, hipStream_t stream);
-}  // namespace fm
 
 namespace {
 
@@ -188,7 +154,7 @@ fm_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
   fm::DsPlan view{};
   if (plan != nullptr) {
     cache = static_cast<char*>(workspace) + need;
-    cap = (long long)((workspace_bytes - need) / (size_t)fm::ds_tile_bytes());
+    cap = (long long)((workspace_bytes - need) / (size_t)fm::DS_TILE_BYTES);
     view = fm::ds_plan_view(plan, B, H, Hm, Nk);
   }
   return from_hip(fm::launch_bwd(dtype == FM_BF16, d, q, k, v, out, dout, lse, dq, dk, dv, dd, lts, lte, uts, ute,
@@ -239,7 +205,7 @@ fm_status fm_bwd_plan(const int32_t* bounds, int B, int H, int Hm, int N, int ca
 
 size_t fm_bwd_ds_workspace_bytes(fm_dtype dtype, int B, int H, int N, int d, int64_t tiles) {
   const size_t base = fm_bwd_workspace_bytes(dtype, B, H, N, d);
-  const size_t tb = (size_t)fm::ds_tile_bytes();
+  const size_t tb = (size_t)fm::DS_TILE_BYTES;
   if (base == 0 || tiles < 0 || (uint64_t)tiles > (SIZE_MAX - base) / tb) return 0;
   return base + (size_t)tiles * tb;
 }

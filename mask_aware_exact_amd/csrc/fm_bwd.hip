@@ -151,11 +151,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
     }
   }
   const float Di = pair_sum(part);
-  float lse2 = INFINITY;  // rows past N or without any unmasked key: exp(S - lse) = 0
+  float lse2 = INFINITY;  // rows past N, without any unmasked key or dropped by qmap: exp(S - lse) = 0
   if (row < Nq) {
-    const float l = a.lse[(size_t)bh * Nq + row];
-    lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
-    if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;
+    if (orow_ok) {
+      const float l = a.lse[(size_t)bh * Nq + row];
+      lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
+    }
+    if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;  // every row's D is written (0 for a dropped row)
   }
   if (d_only) return;
 
@@ -478,12 +480,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // read row N - 1, which gets lse = +inf below and so contributes nothing), lse and D into registers.
   float lr = 0.f, ddr = 0.f;
   int l_row = 0;
+  bool ldrop = false;  // a row whose qmap entry is out of range is dropped: it contributes nothing
   auto fetch_rows = [&](int qt) {
     if (tid < BR) {
       l_row = qt * BR + tid;
       const int i = min(l_row, Nq - 1);
       lr = lseg[i];
       ddr = ddg[i];
+      ldrop = a.qmap != nullptr && (unsigned)a.qmap[(size_t)bh * Nq + i] >= (unsigned)Nq;
     }
   };
   auto fetch = [&](int qt, int qslot, int dslot) {
@@ -494,8 +498,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   };
   auto stash = [&](int ds) {
     if (tid < BR) {
-      // rows past N and rows without any unmasked key (lse = -inf) get +inf: exp(S - lse) = 0 for them
-      const float l = (l_row >= Nq || lr == -INFINITY) ? INFINITY : lr;
+      // rows past N, rows without any unmasked key (lse = -inf) and dropped rows get +inf: exp(S - lse) = 0
+      const float l = (l_row >= Nq || lr == -INFINITY || ldrop) ? INFINITY : lr;
       lse_lds[ds][tid] = l * LOG2E;
       dd_lds[ds][tid] = ddr;
     }
@@ -812,7 +816,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdArgs a) {
     load_tile<float, BR, D, PITCH, Tr::NT>(do_lds, dog, q0, Nq, tid);
     if (tid < BR) {
       const int i = q0 + tid;
-      const float l = i < Nq ? a.lse[(size_t)bh * Nq + i] : INFINITY;
+      const bool drop = i < Nq && a.qmap != nullptr && (unsigned)a.qmap[(size_t)bh * Nq + i] >= (unsigned)Nq;
+      const float l = (i < Nq && !drop) ? a.lse[(size_t)bh * Nq + i] : INFINITY;
       lse_lds[tid] = ((l == -INFINITY) ? INFINITY : l) * LOG2E;
       dd_lds[tid] = i < Nq ? a.dd[(size_t)bh * Nq + i] : 0.f;
     }

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fm_launch.h"
+
 namespace fm {
 
 typedef __bf16 bf16;
@@ -80,22 +82,6 @@ __device__ inline TileBounds merged_bounds(const int* __restrict__ brow, int kt0
   }
   return r;
 }
-
-// Device view of a stored-dS plan (written by the plan pass of the stored-dS backward): per (b, hm, 128-key
-// tile) the first live 64-row query tile and the tile's first slot inside its head's region, per (b, hm)
-// the slots of one head, and per (b, h) the region's first slot. Slots are counted in 16 KB tiles.
-constexpr int DS_QROWS = 64;                         // query rows of a stored dS tile
-constexpr int DS_KEYS = 128;                         // keys of a stored dS tile
-constexpr int DS_TILE_BYTES = DS_QROWS * DS_KEYS * 2;  // bf16
-
-struct DsPlan {
-  long long* total;     // [1]: slots of the whole problem
-  long long* region;    // [B * H]
-  long long* base;      // [B * Hm * nkt]
-  long long* rowtotal;  // [B * Hm]
-  int* first;           // [B * Hm * nkt]
-  int nkt;              // 128-key tiles per row
-};
 
 // Whether head (bh) with mask row mrow has its dS tiles stored: its region fits in the first `cap` slots.
 __device__ __forceinline__ bool ds_head_stored(const DsPlan& p, long long cap, int bh, long long mrow) {

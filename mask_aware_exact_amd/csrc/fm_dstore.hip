@@ -128,27 +128,6 @@ __global__ __launch_bounds__(256) void ds_region_kernel(PlanArgs a) {
   if (threadIdx.x == 0) *a.total = t;
 }
 
-size_t ds_plan_bytes(int B, int H, int Hm, int N) {
-  const size_t nkt = (size_t)(N + DS_KEYS - 1) / DS_KEYS;
-  const size_t rows = (size_t)B * Hm;
-  const size_t bytes = 16 + 8 * ((size_t)B * H + rows * nkt + rows) + 4 * rows * nkt;
-  return (bytes + 255) / 256 * 256;
-}
-
-DsPlan ds_plan_view(const void* plan, int B, int H, int Hm, int N) {
-  const size_t nkt = (size_t)(N + DS_KEYS - 1) / DS_KEYS;
-  const size_t rows = (size_t)B * Hm;
-  char* p = static_cast<char*>(const_cast<void*>(plan));
-  DsPlan v;
-  v.total = reinterpret_cast<long long*>(p);
-  v.region = reinterpret_cast<long long*>(p + 16);
-  v.base = v.region + (size_t)B * H;
-  v.rowtotal = v.base + rows * nkt;
-  v.first = reinterpret_cast<int*>(v.rowtotal + rows);
-  v.nkt = (int)nkt;
-  return v;
-}
-
 hipError_t launch_ds_plan(const int* bounds, int B, int H, int Hm, int N, int causal, void* plan,
                           hipStream_t stream) {
   const DsPlan v = ds_plan_view(plan, B, H, Hm, N);
@@ -170,8 +149,6 @@ hipError_t launch_ds_plan(const int* bounds, int B, int H, int Hm, int N, int ca
   hipLaunchKernelGGL(ds_region_kernel, dim3(1), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
-
-int ds_tile_bytes() { return DS_TILE_BYTES; }
 
 // ------------------------------------------------------------------ dQ from the stored tiles
 

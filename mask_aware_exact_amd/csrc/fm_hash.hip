@@ -27,8 +27,6 @@ constexpr int SORT_T = 1024;   // threads of the sort kernel (16 waves)
 constexpr int SORT_W = SORT_T / 64;
 constexpr int SORT_STAGE = 16;  // chunks of bucket groups staged in LDS at a time
 constexpr int SORT_SEG = 2048;  // least tokens per segment when a head's sort is split over workgroups
-constexpr int LSH_NB_LIMIT = 64;    // largest bucket count of the hash (rotation staged in LDS)
-constexpr int SORT_NB_LIMIT = 512;  // largest bucket count of the sort (per-wave group counts in LDS)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {

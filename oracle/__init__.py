@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CP
 import this package. It shares no code with the HIP path (``mask_aware_exact_amd``) and never imports
 it; the product path never imports this package.
 
-What it computes is the plain definition that the method reaches exactly ("without sacrificing
-computational accuracy", FlashMask abstract, papers.pytorch.kr 2410.01359): the four per-column
+What it computes is the plain definition that the method reaches exactly, since its tile skipping
+costs no accuracy (FlashMask abstract, papers.pytorch.kr 2410.01359): the four per-column
 query-axis boundary vectors are expanded into a dense boolean mask, and softmax attention with its
 gradients is evaluated in float64 with library matrix products and elementwise NumPy operations.
 

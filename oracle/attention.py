@@ -2,10 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see the package header).
 
-The method is exact tiled attention (FlashMask abstract, papers.pytorch.kr 2410.01359: "without
-sacrificing computational accuracy"; FlashAttention-3 abstract, fugumt.com 2407.08608, and the
-FlashAttention README on wenyanet.com describe the exact IO-aware tiling it extends), so the oracle is
-the plain definition, per (batch, head) with rows i and columns j:
+The method is exact tiled attention: skipping masked work loses no accuracy (FlashMask abstract,
+papers.pytorch.kr 2410.01359), and the IO-aware tiling it extends is exact too (FlashAttention-3
+abstract, fugumt.com 2407.08608; the FlashAttention README on wenyanet.com). So the oracle is the plain
+definition, per (batch, head) with rows i and columns j:
 
   S_ij = scale * q_i . k_j, and S_ij = -inf where (i, j) is masked
   P_ij = exp(S_ij - m_i) / l_i,  m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i)

@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY (see the package header).
 
-The method skips tiles the mask covers completely and leaves tiles it does not touch unmasked
-("eliminate unnecessary computations by leveraging sparsity", FlashMask abstract,
+The method skips tiles the mask covers completely and leaves tiles it does not touch unmasked, using
+the mask's sparsity to avoid work that cannot change the result (FlashMask abstract,
 papers.pytorch.kr 2410.01359). The pages give no rule for deciding this; the rule written here is the
 plainest one that the per-column interval representation supports: a tile is FULL when the causal
 triangle or one interval covers every (row, column) of it, NONE when no source can reach any of its

@@ -316,3 +316,13 @@ def test_mapped_out_of_range_entries_write_nothing(fm):
     assert torch.equal(dq2, dq)
     assert torch.equal(dk2[hit_k], dk[hit_k]) and torch.all(dk2[~hit_k] == 7.0)
     assert torch.equal(dv2[hit_k], dv[hit_k]) and torch.all(dv2[~hit_k] == 7.0)
+    # the backward with dropped qmap entries: a dropped query row contributes nothing to dk and dv, which
+    # equal (bit for bit) the full-map run with those rows' dout set to zero; the dq rows named only by
+    # dropped entries keep their previous contents and every other dq row equals the full run's
+    dq3, dk3, dv3 = fm.fm_bwd_mapped(qs, ks, vs, out, dos, lse, qmap, kidx, *vecs, bounds=bounds, causal=False,
+                                     dq=torch.full_like(dq, 7.0))
+    dos0 = torch.where(drop_q[..., None], torch.zeros_like(dos), dos)
+    dq4, dk4, dv4 = fm.fm_bwd_mapped(qs, ks, vs, out, dos0, lse, qidx, kidx, *vecs, bounds=bounds, causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dk3, dk4) and torch.equal(dv3, dv4)
+    assert torch.equal(dq3[hit_q], dq4[hit_q]) and torch.all(dq3[~hit_q] == 7.0)

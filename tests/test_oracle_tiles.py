@@ -91,3 +91,45 @@ def test_causal_exactness_against_dense():
                 blk = m[qt * 64:(qt + 1) * 64, kt * 64:(kt + 1) * 64]
                 assert (cls[qt, kt] == OT.FULL) == bool(blk.all())
                 assert (cls[qt, kt] == OT.NONE) == bool(not blk.any())
+
+
+@pytest.mark.parametrize("qblock", [64, 128])
+@pytest.mark.parametrize("seed", range(4))
+def test_classes_exact_for_tile_aligned_documents(qblock, seed):
+    """With document boundaries on the tile grid the rule is exact in both directions, the interval
+    branches included: FULL exactly where the dense block is all masked, NONE exactly where it has no
+    masked entry (a NONE test that is too strict, e.g. one refusing a tile that ends on the interval's
+    start row, classifies such blocks PARTIAL and fails here)."""
+    rng = np.random.default_rng(100 + seed)
+    N = 1024
+    cuts = np.sort(rng.choice(np.arange(1, N // 128), size=int(rng.integers(1, 5)), replace=False)) * 128
+    bounds = np.concatenate([[0], cuts, [N]])
+    for spec in (W.encode_bidirectional_document(bounds, N), W.encode_causal_document(bounds, N)):
+        m = OM.dense_masked(*spec.column_slice(0, 0), spec.causal, N)
+        cls = OT.tile_classes(OT.tile_bounds(spec.vectors(), 1, 1, N), N, spec.causal, qblock)[0, 0]
+        n_none = 0
+        for qt in range(cls.shape[0]):
+            for kt in range(cls.shape[1]):
+                blk = m[qt * qblock:(qt + 1) * qblock, kt * 64:(kt + 1) * 64]
+                assert (cls[qt, kt] == OT.FULL) == bool(blk.all()), (spec.family, qt, kt)
+                assert (cls[qt, kt] == OT.NONE) == bool(not blk.any()), (spec.family, qt, kt)
+                n_none += int(cls[qt, kt] == OT.NONE)
+        assert n_none > 0
+
+
+def test_exactness_pin_catches_a_too_strict_none_rule(monkeypatch):
+    """Plant the slip the pin above is for (an interval NONE test using r1 < min start instead of
+    r1 <= min start) in the oracle's rule and check that the exactness pin then fails."""
+    real = OT.classify
+
+    def too_strict(r0, r1, c0, c1, bnd, causal):
+        c = real(r0, r1, c0, c1, bnd, causal)
+        mn_lts = int(bnd[0])
+        if c == OT.NONE and r1 == mn_lts:
+            return OT.PARTIAL
+        return c
+
+    monkeypatch.setattr(OT, "classify", too_strict)
+    with pytest.raises(AssertionError):
+        for seed in range(4):
+            test_classes_exact_for_tile_aligned_documents(128, seed)
