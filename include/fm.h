@@ -178,6 +178,21 @@ fm_status fm_bwd_ds(const void* q, const void* k, const void* v, const void* out
                     const int32_t* sched, const void* plan, int causal, float scale, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* fm_bwd that allocates nothing, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments, results and
+ * errors as fm_bwd without the workspace, whose D row term lives instead in a fixed array of
+ * FM_NOALLOC_SCRATCH_BYTES in the library's device memory (one per GPU, held until the process ends).
+ * Limit: B * H * N * 4 <= FM_NOALLOC_SCRATCH_BYTES (B * H * N <= 4194304); larger problems get
+ * FM_ERR_WORKSPACE. Every call on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams) race. Nothing in the array needs clearing: each call writes it before reading it.
+ * FM_ERR_LAUNCH also when the array's address cannot be looked up on the current device. */
+#define FM_NOALLOC_SCRATCH_BYTES (16u << 20)
+fm_status fm_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, fm_dtype dtype, int B, int H, int N, int d, const int32_t* lts,
+                         const int32_t* lte, const int32_t* uts, const int32_t* ute, int Hm, const int32_t* bounds,
+                         const int32_t* sched, int causal, float scale, void* dq, void* dk, void* dv,
+                         hipStream_t stream);
+
 /* One block of query rows against all keys: the unit of work of one rank under context parallelism,
  * whose mask localisation is a zero-communication clip-shift-max on the boundary vectors that keeps the
  * single-GPU kernel (FlashMask-3 summary, readmex.ai, the quoted abstract in the "in-depth insights"

@@ -26,7 +26,7 @@ EXPORTED = ("fm_kblock", "fm_fwd_qblock", "fm_bounds_elems", "fm_tile_bounds", "
             "fm_bwd_workspace_bytes", "fm_bwd", "fm_fwd_rows", "fm_bwd_rows", "fm_tile_classes",
             "fm_compact_keys", "fm_gather_rows", "fm_lsh_buckets", "fm_bucket_sort", "fm_fwd_mapped",
             "fm_bwd_mapped", "fm_bwd_plan_bytes", "fm_bwd_plan", "fm_bwd_ds_workspace_bytes", "fm_bwd_ds",
-            "fm_status_str")
+            "fm_bwd_noalloc", "fm_status_str")
 
 
 class FmError(RuntimeError):
@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH):
     lib.fm_bwd_ds_workspace_bytes.argtypes = [I, I, I, I, I, ctypes.c_int64]
     lib.fm_bwd_ds.restype = I
     lib.fm_bwd_ds.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, P, I, F, P, P, P, P, S, P]
+    lib.fm_bwd_noalloc.restype = I
+    lib.fm_bwd_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, I, P, P, I, F, P, P, P, P]
     lib.fm_tile_classes.restype = I
     lib.fm_tile_classes.argtypes = [P, I, I, I, I, I, P, P]
     lib.fm_fwd_mapped.restype = I
@@ -283,6 +285,26 @@ def fm_bwd_ds(q, k, v, out, dout, lse, plan, lts=None, lte=None, uts=None, ute=N
                          *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), _ptr(plan), int(bool(causal)),
                          float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                          _stream(stream)), "fm_bwd_ds")
+    return dq, dk, dv
+
+
+def fm_bwd_noalloc(q, k, v, out, dout, lse, lts=None, lte=None, uts=None, ute=None, bounds=None, causal=False,
+                   scale=None, dq=None, dk=None, dv=None, stream=None, sched=None):
+    """(dq, dk, dv) as fm_bwd, with the workspace in the library's fixed device array (no allocation
+    inside the call; outputs are allocated here only when not given)."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    vecs = [_vec(x) for x in (lts, lte, uts, ute)]
+    Hm = next((x.shape[1] for x in vecs if x is not None), 1)
+    _need_cuda(q, k, v, out, dout, lse, bounds, sched, *vecs)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib.fm_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q), B, H, N,
+                              d, *[_ptr(x) for x in vecs], Hm, _ptr(bounds), _ptr(sched), int(bool(causal)),
+                              float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)), "fm_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfm.so")
 SOURCES = ["fm_api.hip", "fm_bounds.hip", "fm_fwd.hip", "fm_bwd.hip", "fm_compact.hip", "fm_schedule.hip",
-           "fm_hash.hip", "fm_dstore.hip"]
+           "fm_hash.hip", "fm_dstore.hip", "fm_noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is disabled for all device code; the host pass warns that it does not know

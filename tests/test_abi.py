@@ -247,3 +247,15 @@ def test_hash_validation(lib):
     assert srt(nb=0) == fm.FM_ERR_INVALID
     assert srt(nb=513) == fm.FM_ERR_INVALID
     assert srt(N=(1 << 24) + 1) == fm.FM_ERR_INVALID
+
+
+def test_noalloc_rejects_problems_past_its_array(lib):
+    """fm_bwd_noalloc holds D (4 bytes per query row) in a fixed array of FM_NOALLOC_SCRATCH_BYTES: a larger
+    problem is FM_ERR_WORKSPACE, decided on the host before anything is launched."""
+    limit_rows = (16 << 20) // 4
+    args = lambda H, N: (A, A, A, A, A, A, fm.FM_BF16, 1, H, N, 64, None, None, None, None, 1, None, None, 1,  # noqa
+                         ctypes.c_float(0.125), B_, B_, B_, None)
+    assert lib.fm_bwd_noalloc(*args(64, 131072)) == fm.FM_ERR_WORKSPACE   # 2^23 rows
+    assert lib.fm_bwd_noalloc(*args(32, limit_rows // 32 + 1)) == fm.FM_ERR_WORKSPACE
+    assert lib.fm_bwd_noalloc(*args(2, 0)) == fm.FM_ERR_INVALID            # bad sizes as fm_bwd reports them
+    assert lib.fm_bwd_noalloc(*args(2, 100)[:10] + (96,) + args(2, 100)[11:]) == fm.FM_ERR_UNSUPPORTED
