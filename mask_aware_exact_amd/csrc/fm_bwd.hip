@@ -480,14 +480,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // read row N - 1, which gets lse = +inf below and so contributes nothing), lse and D into registers.
   float lr = 0.f, ddr = 0.f;
   int l_row = 0;
-  bool ldrop = false;  // a row whose qmap entry is out of range is dropped: it contributes nothing
+  int lmap = 0;  // the row's qmap entry: a row whose entry is out of range is dropped (contributes nothing)
   auto fetch_rows = [&](int qt) {
     if (tid < BR) {
       l_row = qt * BR + tid;
       const int i = min(l_row, Nq - 1);
       lr = lseg[i];
       ddr = ddg[i];
-      ldrop = a.qmap != nullptr && (unsigned)a.qmap[(size_t)bh * Nq + i] >= (unsigned)Nq;
+      if (a.qmap != nullptr) lmap = a.qmap[(size_t)bh * Nq + i];
     }
   };
   auto fetch = [&](int qt, int qslot, int dslot) {
@@ -499,6 +499,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   auto stash = [&](int ds) {
     if (tid < BR) {
       // rows past N, rows without any unmasked key (lse = -inf) and dropped rows get +inf: exp(S - lse) = 0
+      const bool ldrop = a.qmap != nullptr && (unsigned)lmap >= (unsigned)Nq;
       const float l = (l_row >= Nq || lr == -INFINITY || ldrop) ? INFINITY : lr;
       lse_lds[ds][tid] = l * LOG2E;
       dd_lds[ds][tid] = ddr;
