@@ -327,6 +327,18 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
   }
 
   if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
+  if constexpr (SWZ && D == 128) {
+    if (a.qmap == nullptr) {
+      // Unmapped bf16 dq: whole rows through LDS (the K tile buffers, free once every wave is here). Not at
+      // d = 64, where the staging code's registers make the kernel spill (it runs at three waves per SIMD).
+      static_assert(sizeof(k_lds) >= 4 * 32 * D * 2, "staging area of four waves");
+      __syncthreads();
+      const int w0 = r0 + wave * 32;
+      store_rows_staged<D>(reinterpret_cast<char*>(&k_lds[0][0]) + wave * (32 * D * 2), acc, a.scale,
+                           static_cast<bf16*>(a.dq) + qhead + (size_t)w0 * D, Nq - w0, lane);
+      return;
+    }
+  }
   // dq = scale * dQ^T for this lane's row.
   if (row < Nq && orow_ok) {
     T* dqg = static_cast<T*>(a.dq) + qhead + (size_t)orow * D;
@@ -712,6 +724,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   if (role == 1 && qs_prev >= 0) dk_pass(q_lds + qs_prev * TILE);
 
   // dV = dV^T (role 0) or dK = scale * dK^T (role 1) for this lane's key column, all of d.
+  if (a.kmap == nullptr) {
+    // Unmapped: whole rows through LDS, role 0 staging in the dO tiles and role 1 in the Q ring, both free
+    // once role 1's last dK products are done and every wave's copies have landed.
+    static_assert(sizeof(do_lds) >= 4 * 32 * D * 2 && sizeof(q_lds) >= 4 * 32 * D * 2, "staging areas");
+    __syncthreads();
+    char* stage = reinterpret_cast<char*>(role == 0 ? do_lds : q_lds) + kgrp * (32 * D * 2);
+    const int k0 = c0 + kgrp * 32;
+    store_rows_staged<D>(stage, acc, role == 0 ? 1.f : a.scale,
+                         static_cast<bf16*>(role == 0 ? a.dv : a.dk) + khead + (size_t)k0 * D, N - k0, lane);
+    return;
+  }
   const int jo = (a.kmap != nullptr && j < N) ? a.kmap[(size_t)bh * N + j] : j;  // the row written
   if (j < N && (unsigned)jo < (unsigned)N) {
     bf16* dst = static_cast<bf16*>(role == 0 ? a.dv : a.dk) + khead + (size_t)jo * D;

@@ -570,4 +570,41 @@ __device__ __forceinline__ void load_tile(T* lds, const T* __restrict__ g, int r
   }
 }
 
+
+// Output rows of one wave, from accumulators in the matrix-core layout (lane l: row l % 32; register r of
+// block db: column 32 db + 8 (r / 4) + 4 (l / 32) + r % 4) to a row-major [*, D] bf16 tensor. Stored
+// directly, each store instruction writes 8 bytes into each of 32 rows, which costs one memory request per
+// 16 bytes. Staged instead through a wave-private LDS area of 32 rows (16-byte chunks XOR-swizzled by row,
+// conflict-free reads), each instruction writes 16 contiguous bytes per lane and whole rows per wave.
+// `mul` scales the lane's own row; rows at or past `nrows` are not stored. `stage` must hold 32 * D bf16
+// (16-byte aligned) that no other wave touches until this returns.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(char* stage, const f32x16 (&acc)[D / 32], float mul,
+                                                  bf16* dst, int nrows, int lane) {
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;     // rows per read instruction
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * q4 + e] * mul);
+      const int c = (4 * db + q4) ^ (l32 & (CH - 1));
+      *reinterpret_cast<bf16x4*>(stage + l32 * (D * 2) + c * 16 + g * 8) = w;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int c = lane % CH;
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / CH;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(stage + rr * (D * 2) + ((c ^ (rr & (CH - 1))) * 16));
+    if (rr < nrows) *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(dst) + (size_t)rr * (D * 2) + c * 16) = v;
+  }
+}
+
 }  // namespace fm

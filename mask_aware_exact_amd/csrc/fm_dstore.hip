@@ -356,20 +356,12 @@ __global__ __launch_bounds__(512, 1) void dq_stream_kernel(DqsArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  // dq = scale * dQ^T for this lane's row.
-  if (row < N) {
-    bf16* dqg = a.dq + (size_t)bh * N * D + (size_t)row * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * q4 + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(dqg + db * 32 + 8 * q4 + 4 * g) = w;
-      }
-    }
-  }
+  // dq = scale * dQ^T, whole rows through LDS (the dS buffers, free once every wave is past its last step).
+  static_assert(sizeof(s_lds) >= 8 * 32 * D * 2, "staging area of eight waves");
+  __syncthreads();
+  const int w0 = r0 + quarter * DS_QROWS + ib * 32;
+  store_rows_staged<D>(&s_lds[0][0][0] + wave * (32 * D * 2), acc, a.scale, a.dq + (size_t)bh * N * D + (size_t)w0 * D,
+                       N - w0, lane);
 }
 
 hipError_t launch_dq_stream(int d, const void* k, const void* ds, long long cap, const DsPlan& plan, void* dq,

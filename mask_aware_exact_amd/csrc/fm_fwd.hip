@@ -69,7 +69,7 @@ struct FwdTraits {
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: unnormalised probabilities stay below 256
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 4 : 2) void fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<T, D>;
   using M = MM<T>;
   constexpr int BR = Tr::BR, BC = Tr::BC, PITCH = Tr::PITCH, CPR = Tr::CPR, CH = Tr::CH;
@@ -116,17 +116,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const bool has_ut = a.uts != nullptr;
   const bool causal = a.causal != 0;
   const float sl2 = a.scale_log2;
-
-  // Q^T operand: lane holds row `row`, k = d in chunks of KW.
-  typename M::frag qf[Tr::NQF];
-#pragma unroll
-  for (int c = 0; c < Tr::NQF; ++c) {
-    if (row < Nq) {
-      qf[c] = load_kcontig_frag<T>(qg + (size_t)row * D + c * M::KW + g * M::E);
-    } else {
-      qf[c] = typename M::frag{};
-    }
-  }
 
   f32x16 o[Tr::NDB];
 #pragma unroll
@@ -202,6 +191,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   TileWindow win = empty_window();
   int kt = next_live_tile(win, 0, kt_end, class_of, lane);
   if (kt < kt_end) fetch(kt, 0);
+  // Q^T operand: lane holds row `row`, k = d in chunks of KW. Loaded after the tile scan and the first
+  // tile's copies, so that the scan waits only for the tile bounds (loads complete in issue order) and the
+  // Q loads travel with the copies.
+  typename M::frag qf[Tr::NQF];
+#pragma unroll
+  for (int c = 0; c < Tr::NQF; ++c) {
+    if (row < Nq) {
+      qf[c] = load_kcontig_frag<T>(qg + (size_t)row * D + c * M::KW + g * M::E);
+    } else {
+      qf[c] = typename M::frag{};
+    }
+  }
   int buf = 0;
   // Loop-invariant parts of the next tile's copies: LDS bases of the tile buffers, and this wave's mask
   // vector (wave w of the first four copies LTS, LTE, UTS, UTE when present).
@@ -338,10 +339,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
   // Epilogue: out = O / l, lse = m_ref * ln2 + ln(l); rows with no unmasked key give 0 and -inf.
   const float l_tot = pair_sum(l_run);
+  const float inv = !(l_tot > 0.f) ? 0.f : 1.f / l_tot;
+  if constexpr (SWZ) {
+    if (a.omap == nullptr) {
+      // Unmapped bf16 output: whole rows through LDS (the K tile buffers, free once every wave is here).
+      static_assert(sizeof(k_lds) >= 4 * 32 * D * 2, "staging area of four waves");
+      __syncthreads();
+      const int w0 = r0 + wave * 32;
+      store_rows_staged<D>(reinterpret_cast<char*>(&k_lds[0][0]) + wave * (32 * D * 2), o, inv,
+                           static_cast<bf16*>(a.out) + qhead + (size_t)w0 * D, Nq - w0, lane);
+      if (row < Nq && g == 0) a.lse[(size_t)bh * Nq + row] = !(l_tot > 0.f) ? -INFINITY : m_ref * LN2 + logf(l_tot);
+      return;
+    }
+  }
   const int orow = (a.omap != nullptr && row < Nq) ? a.omap[(size_t)bh * Nq + row] : row;
   if (row < Nq && (unsigned)orow < (unsigned)Nq) {
-    const bool dead = !(l_tot > 0.f);
-    const float inv = dead ? 0.f : 1.f / l_tot;
     T* og = static_cast<T*>(a.out) + qhead + (size_t)orow * D;
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {

@@ -134,6 +134,51 @@ def test_large_scores_and_rising_maxima(fm, kind, d):
         assert e <= C.TOL["bf16"]["grad"], (name, e)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_key_component_dq_error(d):
+    """A key component rising from -200 to 200 along the key axis (q and the rest of k from the recipe).
+    dQ_i = scale * sum_j dS_ij k_j with sum_j dS_ij = 0, so a large common component of k cancels in exact
+    arithmetic but not in the backward's own precision: D_i = sum_d dO_i * out_i is formed from the bf16
+    output the backward receives, and dS is rounded to bf16 as the operand of the dQ product. Both errors
+    are proportional to |k|. The test measures the GPU's dq error and the error of the oracle's dQ formed
+    with those two roundings (its out rounded to bf16 in D, its dS rounded to bf16), and holds the GPU to
+    1.3 times that floor. out, lse, dk and dv keep their usual bars (out with the half-ulp allowance of
+    the large-score case above)."""
+    import mask_aware_exact_amd as fm
+    from oracle import attention as OA
+    from oracle import masks as OM
+    fm.load_library()
+    base = C.make_case(2, "causal_document", 1, 2, 900, d, "bf16")
+    k = base.k.float()
+    k[..., 0] = torch.linspace(-200.0, 200.0, base.N).view(1, 1, base.N)
+    case = C.Case(f"large-k-d{d}", base.spec, base.B, base.H, base.N, d, "bf16", base.q, k.to(torch.bfloat16),
+                  base.v, base.do)
+    print(f"\ncase {case.name}", flush=True)
+    gpu = C.run_gpu(case, fm)
+    ref = C.run_oracle(case)
+    out_g = gpu["out"].double().numpy()
+    mag = np.maximum(np.abs(ref["out"]), 2.0 ** -126)
+    assert np.all(np.abs(out_g - ref["out"]) <= 1e-2 + np.exp2(np.floor(np.log2(mag)) - 8.0))
+    lse_g = gpu["lse"].double().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert np.max(np.abs(lse_g[fin] - ref["lse"][fin]), initial=0.0) <= C.TOL["bf16"]["lse"]
+    for name in ("dk", "dv"):
+        assert C.rel_fro(gpu[name].double().numpy(), ref[name]) <= C.TOL["bf16"]["grad"], name
+    bf16 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()  # noqa: E731
+    floor_dq = np.zeros_like(ref["dq"])
+    q64, k64, v64, do64 = (C.f64(t) for t in (case.q, case.k, case.v, case.do))
+    for h in range(case.H):
+        masked = OM.dense_masked(*case.spec.column_slice(0, h), case.spec.causal, case.N)
+        r = OA.attend_rows(q64[0, h], k64[0, h], v64[0, h], do64[0, h], masked, case.scale)
+        d_round = (do64[0, h] * bf16(r["out"])).sum(axis=1)
+        ds_round = r["P"] * (do64[0, h] @ v64[0, h].T - d_round[:, None])
+        floor_dq[0, h] = case.scale * (bf16(ds_round) @ k64[0, h])
+    e_gpu = C.rel_fro(gpu["dq"].double().numpy(), ref["dq"])
+    e_floor = C.rel_fro(floor_dq, ref["dq"])
+    print({"d": d, "dq_relF_gpu": e_gpu, "dq_relF_floor": e_floor}, flush=True)
+    assert e_gpu <= 1.3 * e_floor, (e_gpu, e_floor)
+
+
 def test_forward_is_deterministic(fm):
     case = C.make_case(4, "causal_document", 1, 2, 1500, 128, "bf16")
     a, b = C.run_gpu(case, fm), C.run_gpu(case, fm)
