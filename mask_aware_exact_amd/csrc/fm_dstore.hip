@@ -203,7 +203,6 @@ __global__ __launch_bounds__(512, 1) void dq_stream_kernel(DqsArgs a) {
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int g = lane >> 5;
-  const int l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   const int BH = a.B * a.H;
@@ -221,7 +220,6 @@ __global__ __launch_bounds__(512, 1) void dq_stream_kernel(DqsArgs a) {
   const int r0 = qt * QROWS;
   const int r1 = min(N, r0 + QROWS);
   const int quarter = wave >> 1, ib = wave & 1;
-  const int row = r0 + quarter * DS_QROWS + ib * 32 + l32;  // this lane's query row
 
   const bf16* __restrict__ kg = a.k + (size_t)bh * N * D;
   const int* brow = a.bounds == nullptr ? nullptr : a.bounds + mrow * a.nkb * 8;
