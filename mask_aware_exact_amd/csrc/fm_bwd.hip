@@ -374,18 +374,20 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
 // dP_t and the dK products of tile t - 1, whose dS it kept in registers. Phase 2: role 0 issues the dV
 // products of tile t while role 1 forms dS_t. So one wave of a SIMD runs vector arithmetic while the
 // other issues matrix products. Q is kept for three tiles (t - 1, t and the prefetched t + 1).
-template <int D>
+template <int D, int BR_>
 struct PairTraits {
   static constexpr int BC = 128;          // keys per workgroup
-  static constexpr int BR = 64;           // query rows per iteration
+  static constexpr int BR = BR_;          // query rows per iteration (a pair of barriers)
+  static constexpr int NIB = BR / 32;     // 32-row blocks per query tile
   static constexpr int NT = 512;
   static constexpr int NKF = D / 16;      // K or V fragments per lane (k = d)
   static constexpr int NDB = D / 32;      // 32-wide d blocks
 };
 
-template <int D>
+template <int D, int BR_>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
-  using Tr = PairTraits<D>;
+  using Tr = PairTraits<D, BR_>;
+  static_assert(BR_ == 64 || BR_ == 128, "query tiles of 64 or 128 rows");
   using M = MM<bf16>;
   constexpr int BC = Tr::BC, BR = Tr::BR;
   constexpr int TILE = BR * D;
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 do_lds[2 * TILE];
   // P passes from role 0 to role 1 in register order, lane-interleaved: chunk k (4 values) of lane l sits
   // at [group][k][l], so every 8-byte access of a wave is 512 contiguous bytes.
-  __shared__ __attribute__((aligned(16))) bf16x4 p_xch[4][8][64];
+  __shared__ __attribute__((aligned(16))) bf16x4 p_xch[4][Tr::NIB * 4][64];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BR];
   __shared__ __attribute__((aligned(16))) float dd_lds[2][BR];
 
@@ -461,8 +463,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // ds_slot0 + (qt - ds_first) of the cache with four 16-byte stores per lane, each covering 1 KB
   // contiguous: store (ib, p) of lane (g, l32) holds rows 32 ib + 16 p + 4 g + (0..3) and then
   // 32 ib + 16 p + 8 + 4 g + (0..3) of its key, at position g * 32 + (l32 ^ (8 g + 4 p)).
-  static_assert(BC == DS_KEYS && BR == DS_QROWS, "stored dS tiles are the dK/dV pass's tiles");
-  const bool ds_on = role == 1 && ds_stored(a, bh, (long long)b * a.Hm + hm);
+  static_assert(BC == DS_KEYS, "stored dS tiles are the dK/dV pass's tiles");
+  // (stored dS tiles are 64 query rows: a launch with 128-row query tiles never has a cache)
+  const bool ds_on = BR == DS_QROWS && role == 1 && ds_stored(a, bh, (long long)b * a.Hm + hm);
   long long ds_slot0 = 0, ds_span = 0;  // tile qt goes to slot ds_slot0 + (qt - ds_first) when inside the span
   int ds_first = 0;
   int ds_off[2];
@@ -521,12 +524,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // dK^T += Q^T dS for one query tile, dS in register order (role 1). With STORE, the tile's dS also goes
   // to `st` (stored-dS mode), its 4 stores placed after products 1, 3, 5 and 7, so that they leave while
   // the matrix cores work instead of holding up the end of the tile.
-  auto dk_products = [&](auto store_tag, const bf16x4 (&sv)[2][4], const bf16* qb, char* st) {
+  auto dk_products = [&](auto store_tag, const bf16x4 (&sv)[Tr::NIB][4], const bf16* qb, char* st) {
     constexpr bool STORE = decltype(store_tag)::value;
-    constexpr int NM = 4 * Tr::NDB;  // products
+    constexpr int NM = 2 * Tr::NIB * Tr::NDB;  // products
     static_assert(NM >= 8, "a store after every other product");
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2 * Tr::NIB; ++t) {
       bf16x8 sf;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -559,11 +562,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, (8 * Tr::NDB - 4 + NM - 1) / NM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, (2 * NM - 4 + NM - 1) / NM, 0);
         if ((m & 1) && m < 8) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
       }
     } else {
-      interleave_reads<4 * Tr::NDB, 8 * Tr::NDB, 4>();
+      interleave_reads<NM, 2 * NM, 4>();
     }
   };
 
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   if (qt < nq) fetch(qt, 0, 0);
   int qs = 0, ds = 0;     // ring slots of the current tile's Q and dO (and lse / D)
   int qs_prev = -1;       // role 1: slot of the previous tile's Q, whose dS is still pending
-  bf16x4 sv[2][4];        // role 1: that dS, register order
+  bf16x4 sv[Tr::NIB][4];  // role 1: that dS, register order
   char* st_prev = nullptr;  // role 1: that dS's destination in the cache (stored-dS mode), or null
   // dK products of the previous tile, storing its dS on the way when it has a destination
   auto dk_pass = [&](const bf16* qb) {
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     const uint32_t dlds0 = lds_addr(do_lds + (ds ^ 1) * TILE) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
     const char* dgb = reinterpret_cast<const char*>(dog + (size_t)qn * D);
     constexpr int NCP = 2 * TileCopy<D, BR, 8>::NK;  // copies per wave
-    constexpr int NMP = 2 * Tr::NKF;                 // products in the block that carries them
+    constexpr int NMP = Tr::NIB * Tr::NKF;           // products in the block that carries them
     static_assert(NMP % NCP == 0, "copies must spread evenly over the products");
     auto copy_after = [&](int m) {  // after product m (compile-time after unrolling)
       if ((m + 1) % (NMP / NCP) == 0) {
@@ -620,12 +623,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
     // Phase 1. Role 0: S (rows = query rows, columns = this lane's keys) and P, written to LDS.
     // Role 1: dP, then the dK products of the previous tile.
-    bf16x4 pv[2][4];  // P, register order
-    f32x16 x[2];
+    bf16x4 pv[Tr::NIB][4];  // P, register order
+    f32x16 x[Tr::NIB];
     if (role == 0) {
       __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < Tr::NIB; ++ib) {
         x[ib] = zero16();
 #pragma unroll
         for (int c = 0; c < Tr::NKF; ++c) {
@@ -633,15 +636,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
           copy_after(ib * Tr::NKF + c);
         }
       }
-      interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
+      interleave_reads<Tr::NIB * Tr::NKF, Tr::NIB * Tr::NKF, 2>();
       __builtin_amdgcn_s_setprio(0);
       if (need_mask) {
-        const uint64_t mbits =
-            masked_row_bits(qoff + q0, j, qoff + Nq, N, causal, has_lt, has_ut, m_lts, m_lte, m_uts, m_ute);
-        const uint32_t mlo = (uint32_t)(mbits >> (4 * g)), mhi = (uint32_t)(mbits >> (32 + 4 * g));
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const uint32_t mw = ib == 0 ? mlo : mhi;
+        for (int ib = 0; ib < Tr::NIB; ++ib) {
+          // masked-row bits of this lane's key column for the 64 rows holding block ib (two blocks per call)
+          const uint64_t mbits = masked_row_bits(qoff + q0 + 64 * (ib >> 1), j, qoff + Nq, N, causal, has_lt,
+                                                 has_ut, m_lts, m_lte, m_uts, m_ute);
+          const uint32_t mw = (uint32_t)(mbits >> (32 * (ib & 1) + 4 * g));
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
@@ -655,7 +658,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         }
       } else {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
+        for (int ib = 0; ib < Tr::NIB; ++ib) {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
@@ -670,7 +673,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       __builtin_amdgcn_s_setprio(1);
       if (qs_prev >= 0) dk_pass(q_lds + qs_prev * TILE);
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < Tr::NIB; ++ib) {
         x[ib] = zero16();
 #pragma unroll
         for (int c = 0; c < Tr::NKF; ++c) {
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
           copy_after(ib * Tr::NKF + c);
         }
       }
-      interleave_reads<2 * Tr::NKF, 2 * Tr::NKF, 2>();
+      interleave_reads<Tr::NIB * Tr::NKF, Tr::NIB * Tr::NKF, 2>();
       __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();  // (B) P is in LDS
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
     if (role == 0) {
       __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2 * Tr::NIB; ++t) {
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -697,11 +700,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < Tr::NDB; ++db) acc[db] = M::mma(crd.read(dob, t, db), pf, acc[db]);
       }
-      interleave_reads<4 * Tr::NDB, 8 * Tr::NDB, 4>();
+      interleave_reads<2 * Tr::NIB * Tr::NDB, 4 * Tr::NIB * Tr::NDB, 4>();
       __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < Tr::NIB; ++ib) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const bf16x4 p4 = p_xch[kgrp][4 * ib + q4][lane];
@@ -908,7 +911,15 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const long nkt = (a.Nk + 127) / 128;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)(nkt * a.B * a.H)), dim3(512), 0, stream, a);
+    // 128-row query tiles at d = 64 (half the barriers and tile bookkeeping per row; the registers allow
+    // it there), 64-row tiles at d = 128 and whenever dS tiles are stored (their unit is 64 rows).
+    bool tall = false;
+    if constexpr (D == 64) tall = a.ds_cache == nullptr;
+    if (tall) {
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<64, 128>), dim3((unsigned)(nkt * a.B * a.H)), dim3(512), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, 64>), dim3((unsigned)(nkt * a.B * a.H)), dim3(512), 0, stream, a);
+    }
     if (a.ds_cache != nullptr) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
