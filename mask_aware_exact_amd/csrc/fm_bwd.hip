@@ -61,10 +61,14 @@ __device__ __forceinline__ bool ds_stored(const BwdArgs& a, int bh, long long mr
 
 // ------------------------------------------------------------------ 1. dQ (and D), query-tile parallel
 
-template <typename T, int D>
+template <typename T, int D, int BC_ = 64>
 struct DqTraits {
+  static_assert(BC_ == 64 || (BC_ == 128 && sizeof(T) == 2 && D == 64), "128-key tiles: bf16 at d = 64 only");
   static constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
-  static constexpr int BC = 64;   // keys per tile (one bounds entry)
+  static constexpr int BC = BC_;  // keys per tile (BC / 64 bounds entries)
+  static constexpr int NKB = BC / 32;  // 32-key blocks per tile
+  // workgroups per CU: three at d = 64 with 64-key tiles; two when the registers of the larger tiles need it
+  static constexpr int OCC = (sizeof(T) == 2 && D == 64 && BC == 64) ? 3 : 2;
   static constexpr int NT = 256;
   static constexpr bool SWZ = sizeof(T) == 2;            // bf16 K and V tiles: swizzled, unpadded
   static constexpr int KP = SWZ ? D : D + 4;             // row pitch (elements)
@@ -76,9 +80,9 @@ struct DqTraits {
   static constexpr int CH = BC * CPR / NT;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_dq_kernel(BwdArgs a) {
-  using Tr = DqTraits<T, D>;
+template <typename T, int D, int BC_>
+__global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel(BwdArgs a) {
+  using Tr = DqTraits<T, D, BC_>;
   using M = MM<T>;
   constexpr int BR = Tr::BR, BC = Tr::BC, KP = Tr::KP, VP = Tr::VP, CPR = Tr::CPR, CH = Tr::CH;
   constexpr bool SWZ = Tr::SWZ;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
   i32x4 mr = {0, 0, 0, 0};
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto fetch_vectors = [&](int kt, int dst) {
-    copy_tile_vectors(vec_lds[dst], a.lts, a.lte, a.uts, a.ute, vrow, kt * BC, N, wv, lane);
+    copy_tile_vectors<BC>(vec_lds[dst], a.lts, a.lte, a.uts, a.ute, vrow, kt * BC, N, wv, lane);
   };
   auto fetch = [&](int kt, int dst) {
     const int c0 = kt * BC;
@@ -228,7 +232,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
   };
 
   auto class_of = [&](int t) {
-    const TileBounds bt = merged_bounds(brow, t, t + 1, N);
+    constexpr int EPT = BC / KBLOCK;  // bounds entries per tile
+    const TileBounds bt = merged_bounds(brow, t * EPT, min(a.nkb, t * EPT + EPT), N);
     return classify_tile(g0, g1, t * BC, min(N, t * BC + BC), bt, causal);
   };
   TileWindow win = empty_window();
@@ -258,19 +263,19 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
 
     const T* kt_lds = k_lds[buf];
     const T* vt_lds = v_lds[buf];
-    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks (rows = keys, columns = queries). Product
-    // blocks run at raised wave priority, so the two waves of a SIMD drift into opposite phases.
+    // S^T = K Q^T and dP^T = V dO^T for the 32-key blocks of the tile (rows = keys, columns = queries).
+    // Product blocks run at raised wave priority, so the two waves of a SIMD drift into opposite phases.
     __builtin_amdgcn_s_setprio(2);
-    f32x16 s[2], dp[2];
+    f32x16 s[Tr::NKB], dp[Tr::NKB];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < Tr::NKB; ++jb) {
       s[jb] = zero16();
       dp[jb] = zero16();
 #pragma unroll
       for (int c = 0; c < Tr::NQF; ++c) {
         if constexpr (SWZ) {
           constexpr int NC = 2 * TileCopy<D, BC, 4>::NK;  // copies, one after every other product pair
-          static_assert(NC == Tr::NQF, "one copy per two product pairs");
+          static_assert(NC == Tr::NKB * Tr::NQF / 2, "one copy per two product pairs");
           s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
           dp[jb] = M::mma(krd.read(vt_lds, jb, c), df[c], dp[jb]);
           if (c & 1) {
@@ -283,13 +288,14 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
         }
       }
     }
-    interleave_reads<4 * Tr::NQF, 4 * Tr::NQF, 2>();
+    interleave_reads<2 * Tr::NKB * Tr::NQF, 2 * Tr::NKB * Tr::NQF, 2>();
     __builtin_amdgcn_s_setprio(0);
     // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0 (masked scores set to -inf).
     if (need_mask) {
-      tile_column_words(cw_lds[wave], &vec_lds[buf][0][0], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut, lane);
+      tile_column_words<BC>(cw_lds[wave], &vec_lds[buf][0][0], g0 + wave * 32, c0, gend, N, causal, has_lt, has_ut,
+                            lane);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+      for (int jb = 0; jb < Tr::NKB; ++jb) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const i32x4 w4 = column_words4(cw_lds[wave], jb, q4, g);
@@ -299,17 +305,17 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
       }
     }
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < Tr::NKB; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(s[jb][r] * sl2 - lse2);
         dp[jb][r] = p * (dp[jb][r] - Di);
       }
     }
-    // dQ^T += K^T dS^T over the 64 keys of the tile.
+    // dQ^T += K^T dS^T over the keys of the tile.
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-    for (int t = 0; t < 2 * Tr::TPB; ++t) {
+    for (int t = 0; t < Tr::NKB * Tr::TPB; ++t) {
       const typename M::frag sf = acc_frag<T>(dp[t / Tr::TPB], t % Tr::TPB);
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
@@ -320,17 +326,17 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && D == 64) ? 3 : 2) void bwd_
         }
       }
     }
-    interleave_reads<2 * Tr::TPB * Tr::NDB, 4 * Tr::TPB * Tr::NDB, 4>();
+    interleave_reads<Tr::NKB * Tr::TPB * Tr::NDB, 2 * Tr::NKB * Tr::TPB * Tr::NDB, 4>();
     __builtin_amdgcn_s_setprio(0);
     kt = kt_next;
     buf ^= 1;
   }
 
   if constexpr (SWZ) __builtin_amdgcn_s_waitcnt(0);  // the last tile's copies (never read) have landed
-  if constexpr (SWZ && D == 128) {
+  if constexpr (SWZ && (D == 128 || BC == 128)) {
     if (a.qmap == nullptr) {
-      // Unmapped bf16 dq: whole rows through LDS (the K tile buffers, free once every wave is here). Not at
-      // d = 64, where the staging code's registers make the kernel spill (it runs at three waves per SIMD).
+      // Unmapped bf16 dq: whole rows through LDS (the K tile buffers, free once every wave is here). Not with
+      // 64-key tiles at d = 64, where the staging code's registers make the kernel spill (three waves per SIMD).
       static_assert(sizeof(k_lds) >= 4 * 32 * D * 2, "staging area of four waves");
       __syncthreads();
       const int w0 = r0 + wave * 32;
@@ -905,8 +911,10 @@ hipError_t launch_dq_stream(int d, const void* k, const void* ds, long long cap,
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
-  const long nq = (a.Nq + DqTraits<T, D>::BR - 1) / DqTraits<T, D>::BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)(nq * a.B * a.H)), dim3(256), 0, stream, a);
+  // bf16 at d = 64: 128-key tiles (half the barriers per key, as the dK/dV kernel's 128-row tiles there)
+  constexpr int BCQ = (sizeof(T) == 2 && D == 64) ? 128 : 64;
+  const long nq = (a.Nq + DqTraits<T, D, BCQ>::BR - 1) / DqTraits<T, D, BCQ>::BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ>), dim3((unsigned)(nq * a.B * a.H)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long nkt = (a.Nk + 127) / 128;

@@ -209,11 +209,22 @@ __device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int row_end
 // the columns its registers hold. LDS operations of one wave run in order, and the wave-scope fences
 // keep the compiler from moving the read-back above the store. `vec` holds the tile's vectors as
 // int [4][64]: LTS, LTE, UTS, UTE of its 64 columns.
+template <int BCOLS = 64>  // columns of the tile (rows of vec hold BCOLS values each)
 __device__ __forceinline__ void tile_column_words(uint32_t* cw, const int* vec, int q0, int c0, int row_end, int nk,
                                                   bool causal, bool has_lt, bool has_ut, int lane) {
-  const int lts = has_lt ? vec[lane] : 0, lte = has_lt ? vec[64 + lane] : 0;
-  const int uts = has_ut ? vec[128 + lane] : 0, ute = has_ut ? vec[192 + lane] : 0;
-  cw[lane] = masked_row_bits32(q0, c0 + lane, row_end, nk, causal, has_lt, has_ut, lts, lte, uts, ute);
+  if constexpr (BCOLS == 64) {
+    const int lts = has_lt ? vec[lane] : 0, lte = has_lt ? vec[64 + lane] : 0;
+    const int uts = has_ut ? vec[128 + lane] : 0, ute = has_ut ? vec[192 + lane] : 0;
+    cw[lane] = masked_row_bits32(q0, c0 + lane, row_end, nk, causal, has_lt, has_ut, lts, lte, uts, ute);
+  } else {
+#pragma unroll
+    for (int h = 0; h < BCOLS / 64; ++h) {
+      const int c = 64 * h + lane;
+      const int lts = has_lt ? vec[c] : 0, lte = has_lt ? vec[BCOLS + c] : 0;
+      const int uts = has_ut ? vec[2 * BCOLS + c] : 0, ute = has_ut ? vec[3 * BCOLS + c] : 0;
+      cw[c] = masked_row_bits32(q0, c0 + c, row_end, nk, causal, has_lt, has_ut, lts, lte, uts, ute);
+    }
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -498,12 +509,20 @@ __device__ __forceinline__ void copy_vector_slice(int* dst, const int* row, int 
   lds_copy4(row, (uint32_t)min(c0 + lane, n - 1) * 4u, lds_addr(dst));
 }
 
-// One wave per vector: wave w of the first four copies LTS, LTE, UTS, UTE (as present) of the 64 columns
-// from c0 into vec[w][64]. `w` must be wave-uniform.
-__device__ __forceinline__ void copy_tile_vectors(int (*vec)[64], const int* lts, const int* lte, const int* uts,
+// One wave per vector: wave w of the first four copies LTS, LTE, UTS, UTE (as present) of the BCOLS columns
+// from c0 into vec[w][BCOLS], 64 columns per instruction. `w` must be wave-uniform.
+template <int BCOLS = 64>
+__device__ __forceinline__ void copy_tile_vectors(int (*vec)[BCOLS], const int* lts, const int* lte, const int* uts,
                                                   const int* ute, size_t vrow, int c0, int n, int w, int lane) {
   const int* src = w == 0 ? lts : w == 1 ? lte : w == 2 ? uts : ute;
-  if (w < 4 && src != nullptr) copy_vector_slice(vec[w], src + vrow, c0, n, lane);
+  if constexpr (BCOLS == 64) {
+    if (w < 4 && src != nullptr) copy_vector_slice(vec[w], src + vrow, c0, n, lane);
+  } else {
+    if (w < 4 && src != nullptr) {
+#pragma unroll
+      for (int h = 0; h < BCOLS / 64; ++h) copy_vector_slice(vec[w] + 64 * h, src + vrow, c0 + 64 * h, n, lane);
+    }
+  }
 }
 
 // The same copy as copy_tile_async, split into this wave's instructions so that the caller can spread
