@@ -107,6 +107,29 @@ def test_scheduled_results_bitwise_equal(fm, cfg, mask, B, H, N, dtype):
         assert torch.equal(plain[name], sched[name]), name
 
 
+@pytest.mark.parametrize("cfg,mask,B,H,N", [c for c in CASES if c[4] <= 2600])
+def test_scheduled_stored_ds_bitwise_equal(fm, cfg, mask, B, H, N):
+    """fm_bwd_ds with the schedule (its dK/dV units and the D pass in longest-first order) against the same
+    call without: the stored-dS backward only reorders independent units, so dq, dk and dv are equal bit
+    for bit."""
+    print(f"\nscheduled stored-dS cfg{cfg} {mask} B{B} H{H} N{N}", flush=True)
+    case = C.make_case(cfg, mask, B, H, N, 128, "bf16")
+    vecs, bounds, s = _schedule(fm, case.spec, N, N)
+    q, k, v, do = (t.cuda() for t in (case.q, case.k, case.v, case.do))
+    plan = fm.fm_bwd_plan(bounds, B, H, case.spec.Hm, N, case.spec.causal, device=torch.device("cuda"))
+    ws = torch.empty(fm.fm_bwd_ds_workspace_bytes(q.dtype, B, H, N, 128, fm.plan_tiles(plan)), dtype=torch.uint8,
+                     device="cuda")
+    out, lse = fm.fm_fwd(q, k, v, *vecs, bounds=bounds, causal=case.spec.causal, scale=case.scale)
+    res = []
+    for sched in (None, s):
+        grads = fm.fm_bwd_ds(q, k, v, out, do, lse, plan, *vecs, bounds=bounds, sched=sched,
+                             causal=case.spec.causal, scale=case.scale, workspace=ws)
+        torch.cuda.synchronize()
+        res.append([t.cpu() for t in grads])
+    for name, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
+        assert torch.equal(a, b), name
+
+
 def test_scheduled_parity_against_oracle(fm):
     print("\nscheduled parity cfg2 causal_document N1000", flush=True)
     case = C.make_case(2, "causal_document", 2, 2, 1000, 128, "bf16")
