@@ -60,11 +60,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "mask_aware_exact_amd", "csrc", f)
 
 
 def kernel_source_digest() -> str:
+    """Digest of the measured kernels' code: the sources with comments and whitespace removed, so that a
+    comment edit keeps the recorded counters valid while any code change invalidates them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

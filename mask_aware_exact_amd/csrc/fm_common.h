@@ -203,15 +203,17 @@ __device__ __forceinline__ uint32_t masked_row_bits32(int q0, int j, int row_end
   return j >= nk ? ~0u : m;
 }
 
-// Masks of a 64-key tile in the S^T layout (rows = keys in two 32-key blocks, columns = a wave's 32
-// query rows, one row per lane): lane c forms the masked-row word of key column c0 + c for the rows
-// q0 .. q0 + 31 and stores it in the wave's own 64-word LDS row; the wave then reads back the words of
-// the columns its registers hold. LDS operations of one wave run in order, and the wave-scope fences
-// keep the compiler from moving the read-back above the store. `vec` holds the tile's vectors as
-// int [4][64]: LTS, LTE, UTS, UTE of its 64 columns.
-template <int BCOLS = 64>  // columns of the tile (rows of vec hold BCOLS values each)
+// Masks of a tile of BCOLS keys (64 or 128) in the S^T layout (rows = keys in 32-key blocks, columns =
+// a wave's 32 query rows, one row per lane): lane c forms the masked-row word of key columns c0 + c
+// (+ 64, ...) for the rows q0 .. q0 + 31 and stores it in the wave's own BCOLS-word LDS row; the wave then
+// reads back the words of the columns its registers hold. LDS operations of one wave run in order, and
+// the wave-scope fences keep the compiler from moving the read-back above the store. `vec` holds the
+// tile's vectors as int [4][BCOLS]: LTS, LTE, UTS, UTE of its columns.
+template <int BCOLS = 64>
 __device__ __forceinline__ void tile_column_words(uint32_t* cw, const int* vec, int q0, int c0, int row_end, int nk,
                                                   bool causal, bool has_lt, bool has_ut, int lane) {
+  // 64 columns written out as one pass: the loop form of the same arithmetic gives the forward kernel a
+  // different instruction schedule
   if constexpr (BCOLS == 64) {
     const int lts = has_lt ? vec[lane] : 0, lte = has_lt ? vec[64 + lane] : 0;
     const int uts = has_ut ? vec[128 + lane] : 0, ute = has_ut ? vec[192 + lane] : 0;
