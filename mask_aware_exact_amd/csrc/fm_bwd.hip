@@ -394,6 +394,10 @@ template <int D, int BR_>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Tr = PairTraits<D, BR_>;
   static_assert(BR_ == 64 || BR_ == 128, "query tiles of 64 or 128 rows");
+  // With 128-row tiles role 1 forms dP - D in its products (accumulators started at -D, which the D
+  // staging stores negated) instead of subtracting afterwards: BERT-like backward 3-4% faster. With
+  // 64-row tiles the extra loads ahead of the products cost more than the subtractions (+1 to +2%).
+  constexpr bool FOLD_D = BR_ == 128;
   using M = MM<bf16>;
   constexpr int BC = Tr::BC, BR = Tr::BR;
   constexpr int TILE = BR * D;
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       const bool ldrop = a.qmap != nullptr && (unsigned)lmap >= (unsigned)Nq;
       const float l = (l_row >= Nq || lr == -INFINITY || ldrop) ? INFINITY : lr;
       lse_lds[ds][tid] = l * LOG2E;
-      dd_lds[ds][tid] = ddr;
+      dd_lds[ds][tid] = FOLD_D ? -ddr : ddr;
     }
   };
 
@@ -680,7 +684,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       if (qs_prev >= 0) dk_pass(q_lds + qs_prev * TILE);
 #pragma unroll
       for (int ib = 0; ib < Tr::NIB; ++ib) {
-        x[ib] = zero16();
+        if constexpr (FOLD_D) {
+          // dP - D in one pass: the accumulators start at -D of their rows
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 nd4 = *reinterpret_cast<const f32x4*>(&dd_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[ib][4 * q4 + e] = nd4[e];
+          }
+        } else {
+          x[ib] = zero16();
+        }
 #pragma unroll
         for (int c = 0; c < Tr::NKF; ++c) {
           x[ib] = M::mma(rrd.read(dob, ib, c), xf[c], x[ib]);
@@ -714,9 +728,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const bf16x4 p4 = p_xch[kgrp][4 * ib + q4][lane];
-          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
+          if constexpr (FOLD_D) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)p4[e] * (x[ib][4 * q4 + e] - dd4[e]));
+            for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)p4[e] * x[ib][4 * q4 + e]);
+          } else {
+            const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&dd_lds[ds][ib * 32 + 8 * q4 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[ib][q4][e] = (bf16)((float)p4[e] * (x[ib][4 * q4 + e] - dd4[e]));
+          }
         }
       }
       st_prev = (ds_on && qt >= ds_first && (long long)(qt - ds_first) < ds_span)
