@@ -394,10 +394,11 @@ template <int D, int BR_>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   using Tr = PairTraits<D, BR_>;
   static_assert(BR_ == 64 || BR_ == 128, "query tiles of 64 or 128 rows");
-  // With 128-row tiles role 1 forms dP - D in its products (accumulators started at -D, which the D
-  // staging stores negated) instead of subtracting afterwards: BERT-like backward 3-4% faster. With
-  // 64-row tiles the extra loads ahead of the products cost more than the subtractions (+1 to +2%).
-  constexpr bool FOLD_D = BR_ == 128;
+  // At d = 64 role 1 forms dP - D in its products (accumulators started at -D, which the D staging
+  // stores negated) instead of subtracting afterwards: the BERT-like backward 3-4% faster. Both d = 64
+  // tile heights do it, so that fm_bwd and fm_bwd_ds keep identical dK and dV. At d = 128 the loads ahead
+  // of the products cost more than the subtractions (+1 to +2%).
+  constexpr bool FOLD_D = D == 64;
   using M = MM<bf16>;
   constexpr int BC = Tr::BC, BR = Tr::BR;
   constexpr int TILE = BR * D;
