@@ -130,41 +130,24 @@ __global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel
 
   // A head whose dS tiles are stored gets its dq from them later: here it only needs D.
   const bool d_only = ds_stored(a, bh, (long long)b * a.Hm + hm);
-  // Q^T and dO^T operands (k = d) for this lane's row, D_i and lse_i.
-  typename M::frag qf[Tr::NQF], df[Tr::NQF];
-  float part = 0.f;
+  // Q^T and dO^T operands (k = d), O and lse for this lane's row (D_i is formed from them further down).
+  typename M::frag qf[Tr::NQF], df[Tr::NQF], of[Tr::NQF];
   const int orow = (a.qmap != nullptr && row < Nq) ? a.qmap[(size_t)bh * Nq + row] : row;  // out / dq row
   const bool orow_ok = (unsigned)orow < (unsigned)Nq;
+  const float lraw = (row < Nq && orow_ok) ? a.lse[(size_t)bh * Nq + row] : 0.f;
 #pragma unroll
   for (int c = 0; c < Tr::NQF; ++c) {
     if (row < Nq) {
       const size_t e = (size_t)row * D + c * M::KW + g * M::E;
       qf[c] = d_only ? typename M::frag{} : load_kcontig_frag<T>(qg + e);
       df[c] = load_kcontig_frag<T>(dog + e);
-      const typename M::frag of = orow_ok ? load_kcontig_frag<T>(og + (size_t)orow * D + c * M::KW + g * M::E)
-                                          : typename M::frag{};
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) part += (float)df[c][s] * (float)of[s];
-      } else {
-        part += df[c] * of;
-      }
+      of[c] = orow_ok ? load_kcontig_frag<T>(og + (size_t)orow * D + c * M::KW + g * M::E) : typename M::frag{};
     } else {
       qf[c] = typename M::frag{};
       df[c] = typename M::frag{};
+      of[c] = typename M::frag{};
     }
   }
-  const float Di = pair_sum(part);
-  float lse2 = INFINITY;  // rows past N, without any unmasked key or dropped by qmap: exp(S - lse) = 0
-  if (row < Nq) {
-    if (orow_ok) {
-      const float l = a.lse[(size_t)bh * Nq + row];
-      lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
-    }
-    if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;  // every row's D is written (0 for a dropped row)
-  }
-  if (d_only) return;
-
   f32x16 acc[Tr::NDB];
 #pragma unroll
   for (int db = 0; db < Tr::NDB; ++db) acc[db] = zero16();
@@ -236,10 +219,34 @@ __global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel
     const TileBounds bt = merged_bounds(brow, t * EPT, min(a.nkb, t * EPT + EPT), N);
     return classify_tile(g0, g1, t * BC, min(N, t * BC + BC), bt, causal);
   };
+  // The tile scan and the first tile's copies go out before D is formed, so that their round trips overlap
+  // the Q / dO / O loads instead of following them (a D-only head has no tiles).
   TileWindow win = empty_window();
-  int kt = next_live_tile(win, 0, kt_end, class_of, lane);
-  if (kt < kt_end) fetch(kt, 0);
+  int kt = kt_end;
+  if (!d_only) {
+    kt = next_live_tile(win, 0, kt_end, class_of, lane);
+    if (kt < kt_end) fetch(kt, 0);
+  }
   int buf = 0;
+
+  float part = 0.f;
+#pragma unroll
+  for (int c = 0; c < Tr::NQF; ++c) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) part += (float)df[c][s] * (float)of[c][s];
+    } else {
+      part += df[c] * of[c];
+    }
+  }
+  const float Di = pair_sum(part);
+  float lse2 = INFINITY;  // rows past N, without any unmasked key or dropped by qmap: exp(S - lse) = 0
+  if (row < Nq) {
+    if (orow_ok) lse2 = (lraw == -INFINITY) ? INFINITY : lraw * LOG2E;
+    if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;  // every row's D is written (0 for a dropped row)
+  }
+
+  if (d_only) return;
 
   while (kt < kt_end) {
     const int c0 = kt * BC;
