@@ -245,6 +245,26 @@ __global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel
     if (orow_ok) lse2 = (lraw == -INFINITY) ? INFINITY : lraw * LOG2E;
     if (g == 0) a.dd[(size_t)bh * Nq + row] = Di;  // every row's D is written (0 for a dropped row)
   }
+  // bf16 at d = 64: dP^T - D comes out of the products. One more product per 32-key block adds -D_i to
+  // column i: the first operand is 1 at k = 0, 1, 2 for every key, the second holds -D_i split into three
+  // bf16 parts at k = 0, 1, 2 (8 significant bits each: their sum is -D_i to float precision). Four
+  // products per 128-key tile on constant registers in place of 64 subtractions per lane.
+  constexpr bool FOLD_D = SWZ && D == 64;
+  typename M::frag ones_f{}, negd_f{};
+  if constexpr (FOLD_D) {
+    if (g == 0) {
+      const bf16 p0 = (bf16)(-Di);
+      const float r1 = -Di - (float)p0;
+      const bf16 p1 = (bf16)r1;
+      const bf16 p2 = (bf16)(r1 - (float)p1);
+      ones_f[0] = (bf16)1.f;
+      ones_f[1] = (bf16)1.f;
+      ones_f[2] = (bf16)1.f;
+      negd_f[0] = p0;
+      negd_f[1] = p1;
+      negd_f[2] = p2;
+    }
+  }
 
   if (d_only) return;
 
@@ -285,6 +305,9 @@ __global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel
           static_assert(NC == Tr::NKB * Tr::NQF / 2, "one copy per two product pairs");
           s[jb] = M::mma(krd.read(kt_lds, jb, c), qf[c], s[jb]);
           dp[jb] = M::mma(krd.read(vt_lds, jb, c), df[c], dp[jb]);
+          if constexpr (FOLD_D) {
+            if (c == Tr::NQF - 1) dp[jb] = M::mma(ones_f, negd_f, dp[jb]);
+          }
           if (c & 1) {
             const int k = (jb * Tr::NQF + c) >> 1;
             if (k < NC / 2) kcp.issue(k); else vcp.issue(k - NC / 2);
@@ -295,7 +318,7 @@ __global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel
         }
       }
     }
-    interleave_reads<2 * Tr::NKB * Tr::NQF, 2 * Tr::NKB * Tr::NQF, 2>();
+    interleave_reads<2 * Tr::NKB * Tr::NQF + (FOLD_D ? Tr::NKB : 0), 2 * Tr::NKB * Tr::NQF, 2>();
     __builtin_amdgcn_s_setprio(0);
     // dS^T = P^T o (dP^T - D), P^T = exp(S^T - lse) with masked entries 0 (masked scores set to -inf).
     if (need_mask) {
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(256, (DqTraits<T, D, BC_>::OCC)) void bwd_dq_kernel
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(s[jb][r] * sl2 - lse2);
-        dp[jb][r] = p * (dp[jb][r] - Di);
+        dp[jb][r] = FOLD_D ? p * dp[jb][r] : p * (dp[jb][r] - Di);
       }
     }
     // dQ^T += K^T dS^T over the keys of the tile.
