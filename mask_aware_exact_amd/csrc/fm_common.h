@@ -377,29 +377,6 @@ __device__ __forceinline__ int swz_off(int r, int col) {
   return r * (D * 2) + (((col >> 3) ^ swz_key<D>(r)) << 4) + ((col & 7) << 1);
 }
 
-// 8 consecutive elements (k contiguous along the row) from a swizzled tile: col is a multiple of 8.
-template <int D>
-__device__ __forceinline__ bf16x8 swz_kcontig(const bf16* tile, int r, int col) {
-  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + swz_off<D>(r, col));
-}
-
-// load_kmajor_frag for a swizzled tile (see load_kmajor_frag for the k order).
-template <int D>
-__device__ __forceinline__ bf16x8 swz_kmajor(const bf16* tile, int row0, int col0, int t, int lane) {
-  const int g = lane >> 5;
-  const int s = lane & 15;
-  const int col = col0 + (lane & 16) + 4 * (s & 3);
-  const int row = row0 + 16 * t + 4 * g + (s >> 2);
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const char* base = reinterpret_cast<const char*>(tile);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + swz_off<D>(row, col)));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + swz_off<D>(row + 8, col)));
-  bf16x8 f;
-  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-  return f;
-}
-
 // Precomputed per-lane byte offsets for the two read patterns of a swizzled tile. Because swz_key
 // depends only on the low four row bits, moving by 32 rows (row reads) or 16 rows (transposing reads)
 // keeps every offset, so the loops add compile-time row strides to a handful of lane constants.
