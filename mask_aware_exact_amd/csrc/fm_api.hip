@@ -276,6 +276,7 @@ const char* fm_status_str(fm_status s) {
     case FM_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
     case FM_ERR_WORKSPACE: return "workspace missing or too small";
     case FM_ERR_LAUNCH: return "kernel launch failed";
+    default: break;  // the enum's range sentinels and any other value
   }
   return "unknown status";
 }

@@ -52,7 +52,7 @@ __device__ __forceinline__ i32x4 load_cols4(const int* __restrict__ row, int j0,
 template <bool VEC, int TPW>
 __global__ __launch_bounds__(256) void tile_bounds_kernel(const int* __restrict__ lts, const int* __restrict__ lte,
                                                           const int* __restrict__ uts, const int* __restrict__ ute,
-                                                          int rows, int N, int nkt, int nchunks,
+                                                          int N, int nkt, int nchunks,
                                                           int* __restrict__ bounds) {
   const int lane = threadIdx.x & 63;
   const int cpr = (N + BOUNDS_CHUNK - 1) / BOUNDS_CHUNK;  // chunks per row
@@ -137,7 +137,7 @@ hipError_t launch_tile_bounds(const int* lts, const int* lte, const int* uts, co
   const unsigned grid = (unsigned)((waves + 3) / 4);
   auto kern = vec ? (two ? tile_bounds_kernel<true, 2> : tile_bounds_kernel<true, 1>)
                   : (two ? tile_bounds_kernel<false, 2> : tile_bounds_kernel<false, 1>);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, lts, lte, uts, ute, rows, N, nkt, nchunks, bounds);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, lts, lte, uts, ute, N, nkt, nchunks, bounds);
   return hipGetLastError();
 }
 
