@@ -50,7 +50,7 @@ def test_row_blocks_reassemble_the_whole_problem(family, cuts):
 
 
 def test_chunked_head_equals_whole_head():
-    """The row-chunked driver of the full-size checks sums the same float64 terms as fwd_bwd_head."""
+    """The row-chunked form used by the full-size checks sums the same float64 terms as fwd_bwd_head."""
     from concurrent.futures import ThreadPoolExecutor
     from oracle import attention as OA
     import workloads as W
